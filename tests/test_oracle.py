@@ -1,0 +1,418 @@
+"""Pins for the fp64 oracle: closed forms, hand-worked values, invariants,
+brute force, central finite differences and torch fp64 library routines.
+
+Each test is chosen so that a plausible slip in the oracle (a dropped term,
+a wrong sign or index, a transposed operand, an off-by-one window edge, a
+wrong GQA grouping) fails at least one of them.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from transformer_attention_06_amd import synth
+from transformer_attention_06_amd.workload import band_pairs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed):
+    return synth.normal_np(shape, seed).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# forward
+
+
+def test_hand_worked_example():
+    with open(os.path.join(GOLDEN, "hand_attention.json")) as f:
+        g = json.load(f)
+    q = np.array(g["q"], float)[None, :, None, :]
+    k = np.array(g["k"], float)[None, :, None, :]
+    v = np.array(g["v"], float)[None, :, None, :]
+    for case in g["cases"]:
+        out, lse = oracle.attn_fwd(q, k, v, case["window"], math.log(2.0))
+        want = np.array([[float(Fraction(x)) for x in row] for row in case["out"]])
+        np.testing.assert_allclose(out[0, :, 0, :], want, rtol=0, atol=1e-14)
+        want_lse = np.log([float(Fraction(x)) for x in case["lse_exp"]])
+        np.testing.assert_allclose(lse[0, 0], want_lse, rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("T,w", [(1, 1), (7, 3), (12, 5), (64, 16), (64, 63), (33, 32), (100, 1)])
+def test_mask_count_matches_closed_form(T, w):
+    m = oracle.visible_mask(T, w)
+    assert int(m.sum()) == band_pairs(T, w)
+    # brute force membership: i - w < j <= i
+    for i in range(T):
+        for j in range(T):
+            assert m[i, j] == (j <= i and j > i - w)
+
+
+@pytest.mark.parametrize("w", [0, -1, 12, 13, 40])
+def test_window_at_least_T_is_full_causal(w):
+    B, T, H, Hkv, D = 2, 12, 4, 2, 8
+    q, k, v = rnd((B, T, H, D), 1), rnd((B, T, Hkv, D), 2), rnd((B, T, Hkv, D), 3)
+    full_mask = np.tril(np.ones((T, T), bool))
+    assert (oracle.visible_mask(T, w) == full_mask).all()
+    o1, l1 = oracle.attn_fwd(q, k, v, w, 0.3)
+    o2, l2 = oracle.attn_fwd(q, k, v, T, 0.3)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_window_one_returns_v_at_same_position():
+    B, T, H, Hkv, D = 2, 9, 4, 2, 8
+    q, k, v = rnd((B, T, H, D), 4), rnd((B, T, Hkv, D), 5), rnd((B, T, Hkv, D), 6)
+    scale = 0.37
+    out, lse = oracle.attn_fwd(q, k, v, 1, scale)
+    for h in range(H):
+        g = h // (H // Hkv)
+        np.testing.assert_allclose(out[:, :, h, :], v[:, :, g, :], rtol=0, atol=1e-15)
+        np.testing.assert_allclose(lse[:, h, :], scale * (q[:, :, h, :] * k[:, :, g, :]).sum(-1),
+                                   rtol=0, atol=1e-14)
+
+
+@pytest.mark.parametrize("w", [0, 4])
+def test_rows_sum_to_one_and_zero_outside_band(w):
+    B, T, H, Hkv, D = 1, 10, 2, 1, 8
+    q, k = rnd((B, T, H, D), 7), rnd((B, T, Hkv, D), 8)
+    P, _ = oracle.attn_probs(q, k, w, 0.5)
+    np.testing.assert_allclose(P.sum(-1), 1.0, rtol=0, atol=1e-14)
+    mask = oracle.visible_mask(T, w)
+    assert (P[..., ~mask] == 0).all()
+    assert (P[..., mask] > 0).all()
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    B, T, H, Hkv, D = 2, 11, 6, 2, 8
+    G = H // Hkv
+    q, k, v = rnd((B, T, H, D), 9), rnd((B, T, Hkv, D), 10), rnd((B, T, Hkv, D), 11)
+    dout = rnd((B, T, H, D), 12)
+    kr, vr = np.repeat(k, G, axis=2), np.repeat(v, G, axis=2)
+    for w in (0, 3):
+        o1, l1 = oracle.attn_fwd(q, k, v, w, 0.4)
+        o2, l2 = oracle.attn_fwd(q, kr, vr, w, 0.4)
+        np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+        dq1, dk1, dv1 = oracle.attn_bwd(q, k, v, dout, w, 0.4)
+        dq2, dk2, dv2 = oracle.attn_bwd(q, kr, vr, dout, w, 0.4)
+        np.testing.assert_allclose(dq1, dq2, rtol=0, atol=1e-13)
+        # the grouped gradient is the sum of the repeated heads' gradients
+        np.testing.assert_allclose(dk1, dk2.reshape(B, T, Hkv, G, D).sum(3), rtol=0, atol=1e-13)
+        np.testing.assert_allclose(dv1, dv2.reshape(B, T, Hkv, G, D).sum(3), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("w", [0, 5])
+def test_zero_query_gives_uniform_mean(w):
+    B, T, H, Hkv, D = 1, 13, 2, 2, 8
+    q = np.zeros((B, T, H, D))
+    k, v = rnd((B, T, Hkv, D), 13), rnd((B, T, Hkv, D), 14)
+    out, lse = oracle.attn_fwd(q, k, v, w, 0.9)
+    for i in range(T):
+        lo = 0 if w <= 0 else max(0, i - w + 1)
+        n = i - lo + 1
+        np.testing.assert_allclose(out[0, i], v[0, lo:i + 1].mean(0), rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[0, :, i], math.log(n), rtol=0, atol=1e-14)
+
+
+def test_scale_only_multiplies_scores():
+    B, T, H, D = 1, 8, 2, 8
+    q, k, v = rnd((B, T, H, D), 15), rnd((B, T, H, D), 16), rnd((B, T, H, D), 17)
+    o1, l1 = oracle.attn_fwd(q, k, v, 3, 0.25 * 3.0)
+    o2, l2 = oracle.attn_fwd(3.0 * q, k, v, 3, 0.25)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-13)
+
+
+def _torch_sdpa(q, k, v, w, scale):
+    import torch
+    import torch.nn.functional as F
+    T = q.shape[1]
+    mask = torch.from_numpy(_mask_torchless(T, w))
+    qt = torch.from_numpy(q).permute(0, 2, 1, 3)
+    kt = torch.from_numpy(k).permute(0, 2, 1, 3)
+    vt = torch.from_numpy(v).permute(0, 2, 1, 3)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale,
+                                       enable_gqa=(q.shape[2] != k.shape[2]))
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+def _mask_torchless(T, w):
+    # the window rule written independently of the oracle: query i sees the
+    # last min(i+1, w) keys ending at itself
+    m = np.zeros((T, T), bool)
+    for i in range(T):
+        n = i + 1 if (w <= 0 or w >= T) else min(i + 1, w)
+        m[i, i - n + 1:i + 1] = True
+    return m
+
+
+@pytest.mark.parametrize("B,T,H,Hkv,D,w", [(2, 17, 4, 2, 8, 0), (1, 32, 4, 1, 16, 7), (2, 9, 3, 3, 4, 2)])
+def test_forward_matches_torch_fp64_sdpa(B, T, H, Hkv, D, w):
+    q, k, v = rnd((B, T, H, D), 18), rnd((B, T, Hkv, D), 19), rnd((B, T, Hkv, D), 20)
+    out, _ = oracle.attn_fwd(q, k, v, w, 0.3)
+    np.testing.assert_allclose(out, _torch_sdpa(q, k, v, w, 0.3), rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# backward
+
+
+def _loss(q, k, v, dout, w, scale):
+    return float((oracle.attn_fwd(q, k, v, w, scale)[0] * dout).sum())
+
+
+@pytest.mark.parametrize("w", [0, 3])
+def test_backward_central_differences_every_coordinate(w):
+    B, T, H, Hkv, D = 1, 8, 2, 1, 8
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = rnd((B, T, H, D), 21), rnd((B, T, Hkv, D), 22), rnd((B, T, Hkv, D), 23)
+    dout = rnd((B, T, H, D), 24)
+    grads = oracle.attn_bwd(q, k, v, dout, w, scale)
+    eps = 1e-6
+    for which, (x, gx) in enumerate(zip((q, k, v), grads)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            args = [q.copy(), k.copy(), v.copy()]
+            args[which][idx] += eps
+            lp = _loss(*args, dout, w, scale)
+            args[which][idx] -= 2 * eps
+            lm = _loss(*args, dout, w, scale)
+            fd[idx] = (lp - lm) / (2 * eps)
+        err = np.abs(fd - gx).max() / max(1e-12, np.abs(gx).max())
+        assert err < 1e-6, (which, err)
+
+
+def test_backward_sums_over_keys():
+    B, T, H, Hkv, D = 2, 14, 4, 2, 8
+    q, k, v = rnd((B, T, H, D), 25), rnd((B, T, Hkv, D), 26), rnd((B, T, Hkv, D), 27)
+    dout = rnd((B, T, H, D), 28)
+    for w in (0, 4):
+        dq, dk, dv = oracle.attn_bwd(q, k, v, dout, w, 0.35)
+        # softmax rows sum to one, so dS rows sum to zero: sum_j dK_j = 0
+        np.testing.assert_allclose(dk.sum(1), 0.0, rtol=0, atol=1e-12)
+        # and sum_j dV_j = sum over the group's heads and all queries of dout
+        G = H // Hkv
+        np.testing.assert_allclose(dv.sum(1), dout.reshape(B, T, Hkv, G, D).sum((1, 3)), rtol=0, atol=1e-12)
+
+
+def test_backward_window_one_closed_form():
+    B, T, H, Hkv, D = 1, 6, 4, 2, 8
+    q, k, v = rnd((B, T, H, D), 29), rnd((B, T, Hkv, D), 30), rnd((B, T, Hkv, D), 31)
+    dout = rnd((B, T, H, D), 32)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, dout, 1, 0.5)
+    assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+    np.testing.assert_allclose(dv, dout.reshape(B, T, Hkv, 2, D).sum(3), rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("B,T,H,Hkv,D,w", [(2, 13, 4, 2, 8, 0), (1, 20, 2, 1, 16, 6)])
+def test_backward_matches_torch_fp64_autograd(B, T, H, Hkv, D, w):
+    import torch
+    import torch.nn.functional as F
+    q, k, v = rnd((B, T, H, D), 33), rnd((B, T, Hkv, D), 34), rnd((B, T, Hkv, D), 35)
+    dout = rnd((B, T, H, D), 36)
+    qt, kt, vt = (torch.from_numpy(x).permute(0, 2, 1, 3).clone().requires_grad_(True) for x in (q, k, v))
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=torch.from_numpy(_mask_torchless(T, w)),
+                                       scale=0.3, enable_gqa=(H != Hkv))
+    o.backward(torch.from_numpy(dout).permute(0, 2, 1, 3))
+    dq, dk, dv = oracle.attn_bwd(q, k, v, dout, w, 0.3)
+    for mine, ref in ((dq, qt), (dk, kt), (dv, vt)):
+        np.testing.assert_allclose(mine, ref.grad.permute(0, 2, 1, 3).numpy(), rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# decode
+
+
+def test_decode_equals_last_row_of_prefill():
+    B, T_max, H, Hkv, D = 4, 24, 4, 2, 8
+    kc, vc = rnd((B, T_max, Hkv, D), 37), rnd((B, T_max, Hkv, D), 38)
+    q = rnd((B, H, D), 39)
+    lens = np.array([1, 7, 24, 13])
+    for w in (0, 5, 1, 30):
+        out, lse = oracle.decode(q, kc, vc, lens, w, 0.3)
+        for b in range(B):
+            L = lens[b]
+            qp = np.zeros((1, L, H, D))
+            qp[0, L - 1] = q[b]
+            o, l = oracle.attn_fwd(qp, kc[b:b + 1, :L], vc[b:b + 1, :L], w, 0.3)
+            np.testing.assert_allclose(out[b], o[0, L - 1], rtol=0, atol=1e-14)
+            np.testing.assert_allclose(lse[b], l[0, :, L - 1], rtol=0, atol=1e-14)
+
+
+def test_decode_length_one_and_poisoned_cache():
+    B, T_max, H, Hkv, D = 3, 16, 2, 1, 8
+    kc, vc = rnd((B, T_max, Hkv, D), 40), rnd((B, T_max, Hkv, D), 41)
+    q = rnd((B, H, D), 42)
+    lens = np.array([1, 9, 16])
+    w = 4
+    out, lse = oracle.decode(q, kc, vc, lens, w, 0.7)
+    np.testing.assert_allclose(out[0], np.repeat(vc[0, 0], H, 0), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(lse[0], 0.7 * (q[0] @ kc[0, 0, 0]), rtol=0, atol=1e-14)
+    kp, vp = kc.copy(), vc.copy()
+    for b, L in enumerate(lens):
+        kp[b, L:] = np.nan
+        vp[b, L:] = np.nan
+        kp[b, :max(0, L - w)] = np.nan
+        vp[b, :max(0, L - w)] = np.nan
+    out2, lse2 = oracle.decode(q, kp, vp, lens, w, 0.7)
+    assert np.isfinite(out2).all() and np.isfinite(lse2).all()
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_decode_matches_torch_fp64_sdpa():
+    import torch
+    import torch.nn.functional as F
+    B, T_max, H, Hkv, D = 3, 20, 6, 2, 16
+    kc, vc = rnd((B, T_max, Hkv, D), 43), rnd((B, T_max, Hkv, D), 44)
+    q = rnd((B, H, D), 45)
+    lens = np.array([20, 3, 11])
+    w = 6
+    out, _ = oracle.decode(q, kc, vc, lens, w, 0.2)
+    for b, L in enumerate(lens):
+        lo = max(0, L - w)
+        o = F.scaled_dot_product_attention(
+            torch.from_numpy(q[b])[:, None, :], torch.from_numpy(kc[b, lo:L]).permute(1, 0, 2),
+            torch.from_numpy(vc[b, lo:L]).permute(1, 0, 2), scale=0.2, enable_gqa=True)
+        np.testing.assert_allclose(out[b], o[:, 0, :].numpy(), rtol=0, atol=1e-13)
+
+
+# ----------------------------------------------------------------------------
+# prologue
+
+
+def test_inv_freq_golden():
+    with open(os.path.join(GOLDEN, "rope_inv_freq.json")) as f:
+        g = json.load(f)
+    np.testing.assert_allclose(oracle.inv_freq(g["D"], g["base"]), g["inv_freq"], rtol=1e-15, atol=0)
+
+
+def test_rope_position_zero_is_identity_and_d2_is_plane_rotation():
+    x = rnd((2, 1, 3, 16), 46)
+    np.testing.assert_array_equal(oracle.rope_rotate(x, np.zeros((2, 1), int)), x)
+    # D = 2: the single pair rotates by p radians (inv_freq_0 = 1)
+    e1 = np.zeros((1, 5, 1, 2))
+    e1[..., 0] = 1.0
+    pos = np.arange(5)[None, :]
+    y = oracle.rope_rotate(e1, pos)
+    np.testing.assert_allclose(y[0, :, 0, 0], np.cos(np.arange(5)), rtol=0, atol=1e-15)
+    np.testing.assert_allclose(y[0, :, 0, 1], np.sin(np.arange(5)), rtol=0, atol=1e-15)
+
+
+def test_rope_preserves_norm_and_is_relative():
+    D = 32
+    q, k = rnd((1, 40, 1, D), 47), rnd((1, 40, 1, D), 48)
+    pos = np.arange(40)[None, :]
+    rq, rk = oracle.rope_rotate(q, pos), oracle.rope_rotate(k, pos)
+    np.testing.assert_allclose(np.linalg.norm(rq, axis=-1), np.linalg.norm(q, axis=-1), rtol=1e-14)
+    s1 = rq[0, :, 0] @ rk[0, :, 0].T
+    rq2, rk2 = oracle.rope_rotate(q, pos + 37), oracle.rope_rotate(k, pos + 37)
+    s2 = rq2[0, :, 0] @ rk2[0, :, 0].T
+    np.testing.assert_allclose(s1, s2, rtol=0, atol=1e-12)
+    # and the scores do depend on the offset between query and key
+    rk3 = oracle.rope_rotate(k, pos + 1)
+    assert np.abs(rq[0, :, 0] @ rk3[0, :, 0].T - s1).max() > 1e-3
+
+
+def test_rope_half_split_pairs_and_sign():
+    # rotating e_d (d < D/2) by theta moves it into e_{d+D/2} with +sin
+    D = 8
+    x = np.zeros((1, 1, 1, D))
+    x[..., 1] = 1.0
+    th = 3 * 100000.0 ** (-2.0 / D)
+    y = oracle.rope_rotate(x, np.array([[3]]))
+    want = np.zeros(D)
+    want[1], want[1 + D // 2] = math.cos(th), math.sin(th)
+    np.testing.assert_allclose(y[0, 0, 0], want, rtol=0, atol=1e-15)
+
+
+def test_rms_norm_matches_torch_and_closed_form():
+    import torch
+    import torch.nn.functional as F
+    x = rnd((3, 5, 2, 32), 49)
+    eps = 2.0 ** -23
+    y = oracle.rms_norm(x, eps)
+    np.testing.assert_allclose(y, F.rms_norm(torch.from_numpy(x), (32,), eps=eps).numpy(), rtol=0, atol=1e-14)
+    ms = (x * x).mean(-1)
+    np.testing.assert_allclose((y * y).sum(-1), 32 * ms / (ms + eps), rtol=1e-13)
+
+
+def test_norm_and_rope_commute():
+    x = rnd((2, 6, 3, 16), 50)
+    pos = np.arange(6)[None, :] + np.array([[0], [100]])
+    a = oracle.rope_rotate(oracle.rms_norm(x, 1e-6), pos)
+    b = oracle.rms_norm(oracle.rope_rotate(x, pos), 1e-6)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+
+
+def test_prologue_backward_central_differences_and_torch():
+    import torch
+    import torch.nn.functional as F
+    B, T, H, Hkv, D = 1, 5, 2, 1, 8
+    eps = 2.0 ** -23
+    q, k = rnd((B, T, H, D), 51), rnd((B, T, Hkv, D), 52)
+    dqo, dko = rnd((B, T, H, D), 53), rnd((B, T, Hkv, D), 54)
+    pos = oracle.positions_from_offsets(B, T, [3])
+    dq, dk = oracle.qk_prologue_bwd(q, k, pos, dqo, dko, eps)
+
+    def L(qq, kk):
+        a, b = oracle.qk_prologue_fwd(qq, kk, pos, eps)
+        return float((a * dqo).sum() + (b * dko).sum())
+
+    h = 1e-6
+    for x, gx, which in ((q, dq, 0), (k, dk, 1)):
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            if which == 0:
+                fd[idx] = (L(xp, k) - L(xm, k)) / (2 * h)
+            else:
+                fd[idx] = (L(q, xp) - L(q, xm)) / (2 * h)
+        assert np.abs(fd - gx).max() / np.abs(gx).max() < 1e-7
+    # torch autograd through torch's own rms_norm and a rotation built from torch.cos/sin
+    xt = torch.from_numpy(q).clone().requires_grad_(True)
+    n = F.rms_norm(xt, (D,), eps=eps)
+    th = torch.from_numpy(pos.astype(np.float64))[:, :, None, None] * torch.from_numpy(oracle.inv_freq(D))
+    a, b = n[..., :D // 2], n[..., D // 2:]
+    y = torch.cat([a * torch.cos(th) - b * torch.sin(th), a * torch.sin(th) + b * torch.cos(th)], -1)
+    y.backward(torch.from_numpy(dqo))
+    np.testing.assert_allclose(dq, xt.grad.numpy(), rtol=0, atol=1e-12)
+
+
+def test_tiny_end_to_end_gradients_through_prologue():
+    """Central differences through prologue + attention on the tiny workload's
+    geometry (B=1, H=2, Hkv=1, D=32) at a shorter length, sampled coordinates."""
+    B, T, H, Hkv, D = 1, 16, 2, 1, 32
+    eps, scale = 2.0 ** -23, 1.0 / math.sqrt(32)
+    q, k, v = rnd((B, T, H, D), 55), rnd((B, T, Hkv, D), 56), rnd((B, T, Hkv, D), 57)
+    dout = rnd((B, T, H, D), 58)
+    pos = oracle.positions_from_offsets(B, T)
+    for w in (4, 0):
+        qp, kp = oracle.qk_prologue_fwd(q, k, pos, eps)
+        dqp, dkp, dv = oracle.attn_bwd(qp, kp, v, dout, w, scale)
+        dq, dk = oracle.qk_prologue_bwd(q, k, pos, dqp, dkp, eps)
+
+        def L(qq, kk, vv):
+            a, b = oracle.qk_prologue_fwd(qq, kk, pos, eps)
+            return float((oracle.attn_fwd(a, b, vv, w, scale)[0] * dout).sum())
+
+        rng = np.random.default_rng(59)
+        h = 1e-6
+        for which, (x, gx) in enumerate(((q, dq), (k, dk), (v, dv))):
+            for _ in range(24):
+                idx = tuple(int(rng.integers(0, s)) for s in x.shape)
+                args = [q.copy(), k.copy(), v.copy()]
+                args[which][idx] += h
+                lp = L(*args)
+                args[which][idx] -= 2 * h
+                lm = L(*args)
+                fd = (lp - lm) / (2 * h)
+                assert abs(fd - gx[idx]) <= 1e-6 * max(1.0, abs(gx[idx])), (which, idx, fd, gx[idx])
