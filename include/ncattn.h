@@ -1,0 +1,179 @@
+/*
+ * libncattn — nanochat's attention hot path for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Every tensor argument is a plain device pointer to memory the caller
+ * owns (any HIP device allocation on the current device); sizes are plain
+ * ints. The library allocates no device memory, keeps no per-call state and
+ * never synchronises: every entry point validates its arguments on the host,
+ * enqueues its kernels on the caller's stream and returns. Results are
+ * available once the stream has reached that point.
+ *
+ * Layouts (row-major, innermost dimension last, fully contiguous):
+ *   q, out, dq, dout      [B, T, H,   D]
+ *   k, v, dk, dv          [B, T, Hkv, D]
+ *   lse, delta            [B, H, T]  float32, natural log
+ *   decode q, out         [B, H, D];  decode lse [B, H] float32
+ *   decode caches         [B, T_max, Hkv, D]  (one layer's slab of a
+ *                          (n_layers, B, T_max, Hkv, D) cache)
+ * Element type of q/k/v/out/gradients/caches is given by nc_dtype; lse,
+ * RoPE tables and workspaces are float32.
+ *
+ * Grouped-query attention: query head h reads key/value head h / (H / Hkv)
+ * ("nanochat Admin & Developer Guide", section 3: n_kv_head <= n_head;
+ * section 6: GQA through KV heads repeated in place).
+ *
+ * Window: key j is visible to query i iff i - window < j <= i, i.e. window
+ * counts the keys a query sees including itself; window <= 0 or
+ * window >= T means full causal attention (section 3, "Sliding-window
+ * attention": per-layer windows handed to the kernel as (left, right)
+ * tuples; a (left, 0) tuple is window = left + 1).
+ *
+ * Errors: validation happens before any HIP call and before any output is
+ * touched; on an error nothing is launched and the outputs keep their
+ * contents. nc_last_error_message() gives a per-thread description of the
+ * last error. Requirements checked: non-null pointers, sizes >= 1,
+ * H % Hkv == 0, D in {32, 64, 128}, a known dtype, 16-byte aligned tensor
+ * pointers, element counts below 2^31, sufficient workspace, and a gfx950
+ * current device (NC_ERR_DEVICE otherwise). A launch failure reported by the
+ * runtime gives NC_ERR_LAUNCH; outputs are then undefined. Outputs must not
+ * alias inputs. All entry points are thread-safe and reentrant.
+ */
+#ifndef NCATTN_H
+#define NCATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NCATTN_ABI_VERSION 1
+
+typedef enum {
+  NC_OK = 0,
+  NC_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, bad window/scale */
+  NC_ERR_UNSUPPORTED = 2, /* valid but not built: head dim, dtype, size limit */
+  NC_ERR_WORKSPACE = 3,   /* workspace pointer null or smaller than required */
+  NC_ERR_DEVICE = 4,      /* no device, or the current device is not gfx950 */
+  NC_ERR_LAUNCH = 5       /* the runtime reported an error after a launch */
+} nc_status;
+
+typedef enum { NC_F32 = 0, NC_BF16 = 1 } nc_dtype;
+
+/* A hipStream_t (NULL = the default stream); kept opaque so that callers do
+ * not need HIP headers. */
+typedef void* nc_stream;
+
+int nc_abi_version(void);
+const char* nc_status_string(nc_status s);
+/* Description of the last error on the calling thread ("" if none). */
+const char* nc_last_error_message(void);
+
+/*
+ * Attention forward.
+ * Computes, per (b, h) with g = h / (H / Hkv) and s_ij = scale * <q_i, k_j>:
+ *   lse_i = ln sum_{j visible} exp(s_ij),  out_i = sum_{j visible} exp(s_ij - lse_i) v_j.
+ * Defined by "nanochat Admin & Developer Guide", section 3 (causal GQA with
+ * per-layer sliding windows) and section 6 (the FA3 / SDPA attention call).
+ * bf16: inputs bf16, products on bf16 matrix cores with float32 accumulation,
+ * softmax statistics in float32, probabilities rounded to bf16 before the
+ * P.V product, out rounded to nearest even. f32: float32 throughout.
+ *   q [B,T,H,D], k/v [B,T,Hkv,D] (dtype dt)  -> out [B,T,H,D] (dt), lse [B,H,T] (f32)
+ * scale must be finite and > 0.
+ */
+nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
+                      const void* q, const void* k, const void* v,
+                      int window, float scale,
+                      void* out, float* lse, nc_stream stream);
+
+/*
+ * Attention backward: gradients of L = sum(out * dout) w.r.t. q, k, v, with
+ * P recomputed from the saved lse. Per (b, h):
+ *   dP_ij = <dout_i, v_j>, delta_i = <dout_i, out_i>,
+ *   dS_ij = P_ij (dP_ij - delta_i),
+ *   dq_i = scale sum_j dS_ij k_j,
+ *   dk_j = scale sum_{h in group} sum_i dS_ij q_i,
+ *   dv_j = sum_{h in group} sum_i P_ij dout_i.
+ * dk/dv are summed over the query heads of each group. dq/dk/dv are fully
+ * overwritten. q, k, v, out, lse must be those of nc_attn_fwd with the same
+ * window and scale. The float32 workspace holds delta [B,H,T] and a dq
+ * accumulator [B,T,H,D]; its size is nc_attn_bwd_workspace_bytes().
+ * dq accumulation uses float32 atomics, so dq can differ in the last bits
+ * between runs; dk and dv are deterministic.
+ */
+size_t nc_attn_bwd_workspace_bytes(nc_dtype dt, int B, int T, int H, int Hkv, int D);
+nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
+                      const void* q, const void* k, const void* v,
+                      const void* out, const float* lse, const void* dout,
+                      int window, float scale,
+                      void* dq, void* dk, void* dv,
+                      void* workspace, size_t workspace_bytes, nc_stream stream);
+
+/*
+ * Single-token decode against one layer's KV cache ("nanochat Admin &
+ * Developer Guide", section 7 "KV cache": per-layer (B, T, H, D) cache with
+ * int32 per-row lengths; section 6: single-token decode slices the key
+ * window). Row b holds seqlens[b] cached keys including the current token,
+ * whose query sits at position seqlens[b] - 1; it sees cache positions
+ * max(0, seqlens[b] - window) .. seqlens[b] - 1 (all of them when
+ * window <= 0 or window >= seqlens[b]). Positions outside that range are never
+ * read. seqlens is a DEVICE int32 array [B]; values outside 1..T_max cannot
+ * be checked without a sync, so such a row's out and lse are written as NaN.
+ *   q [B,H,D], k_cache/v_cache [B,T_max,Hkv,D], seqlens [B]
+ *   -> out [B,H,D], lse [B,H]
+ * The float32 workspace holds split-K partials; size from
+ * nc_attn_decode_workspace_bytes().
+ */
+size_t nc_attn_decode_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, int D, int T_max);
+nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max,
+                         const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* seqlens, int window, float scale,
+                         void* out, float* lse,
+                         void* workspace, size_t workspace_bytes, nc_stream stream);
+
+/*
+ * RoPE table: cos_out[p, d] = cos(p * base^(-2d/D)), sin_out likewise, for
+ * p in 0..T_rope-1 and d in 0..D/2-1, float32 [T_rope, D/2]. Angles and the
+ * trigonometry are evaluated in float64 on the device, then rounded to
+ * float32. ("nanochat Admin & Developer Guide", section 3: rotary
+ * embeddings with base 100000, table over-computed past the sequence
+ * length; "nanochat (Fucina port)", "Architecture": table built from the
+ * inverse frequencies.) base must be > 1; D even, 2..256.
+ */
+nc_status nc_rope_table(int T_rope, int D, double base,
+                        float* cos_out, float* sin_out, nc_stream stream);
+
+/*
+ * QK prologue forward: for every head vector x (of q and of k) at position
+ * p = (pos_offset ? pos_offset[b] : 0) + t:
+ *   y = x / sqrt(mean_d x_d^2 + eps)                (RMSNorm, no weight)
+ *   (y_d, y_{d+D/2}) <- (y_d c - y_{d+D/2} s, y_d s + y_{d+D/2} c),  d < D/2,
+ *   c = cos[p, d], s = sin[p, d]                    (half-split RoPE)
+ * ("nanochat Admin & Developer Guide", section 3: QK-norm without learnable
+ * parameters, RoPE; "nanochat (Fucina port)", "Architecture"). Statistics in
+ * float32. pos_offset is a DEVICE int32 array [B] or NULL; a position
+ * outside 0..T_rope-1 writes NaN for that vector.
+ *   q [B,T,H,D], k [B,T,Hkv,D] -> q_out, k_out (same shape and dtype)
+ */
+nc_status nc_qk_prologue_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
+                             const void* q, const void* k, const int32_t* pos_offset,
+                             const float* cos_tab, const float* sin_tab, int T_rope,
+                             float eps, void* q_out, void* k_out, nc_stream stream);
+
+/*
+ * QK prologue backward: given dq_out, dk_out (gradients w.r.t. the prologue
+ * outputs) and the raw q, k, writes dq, dk w.r.t. the raw inputs:
+ *   u = R(-theta) dy,  r = sqrt(mean x^2 + eps),  dx = u / r - x <x, u> / (D r^3).
+ */
+nc_status nc_qk_prologue_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
+                             const void* q, const void* k, const int32_t* pos_offset,
+                             const float* cos_tab, const float* sin_tab, int T_rope,
+                             float eps, const void* dq_out, const void* dk_out,
+                             void* dq, void* dk, nc_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NCATTN_H */

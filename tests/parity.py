@@ -1,0 +1,43 @@
+"""Helpers shared by the GPU parity tests (tolerances, metrics, inputs)."""
+
+import numpy as np
+
+from transformer_attention_06_amd import synth
+
+# Tolerances: float32 configurations max-abs <= 1e-4; bfloat16 rel-L2 <= 5e-3
+# on out and <= 1e-2 on dq/dk/dv; lse max-abs <= 1e-3 (bf16) / 1e-4 (f32).
+TOL = {
+    "f32": dict(out=("maxabs", 1e-4), lse=("maxabs", 1e-4), grad=("maxabs", 1e-4)),
+    "bf16": dict(out=("rel_l2", 5e-3), lse=("maxabs", 1e-3), grad=("rel_l2", 1e-2)),
+}
+
+
+def rel_l2(x, ref):
+    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    return float(np.linalg.norm((x - ref).ravel()) / max(np.linalg.norm(ref.ravel()), 1e-300))
+
+
+def max_abs(x, ref):
+    return float(np.abs(np.asarray(x, np.float64) - np.asarray(ref, np.float64)).max())
+
+
+def check(name, got, ref, dtype, kind):
+    metric, tol = TOL[dtype][kind]
+    got = np.asarray(got, np.float64)
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    if metric == "rel_l2" and not np.any(ref):
+        # degenerate case whose exact result is identically zero (one visible
+        # key, window 1): relative error is undefined, bound the absolute one
+        metric, tol = "maxabs", 1e-4
+    err = rel_l2(got, ref) if metric == "rel_l2" else max_abs(got, ref)
+    assert err <= tol, f"{name}: {metric} {err:.3e} > {tol:.1e}"
+    return err
+
+
+def inputs(shapes, seed, dtype, device="cuda"):
+    """Seeded N(0,1) tensors on the device (numpy PCG64, RNE-cast)."""
+    return [synth.normal_torch(s, seed + i, dtype, device) for i, s in enumerate(shapes)]
+
+
+def f64(t):
+    return synth.to_f64(t)

@@ -1,0 +1,175 @@
+"""The C-ABI library loads without a GPU, exports every declared symbol, and
+rejects every invalid argument with its status code before any HIP call.
+No test here launches a kernel: all pointers are fake addresses that the
+validation must reject before they could be used."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from transformer_attention_06_amd import native
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE, DEVICE = 0, 1, 2, 3, 4
+F32, BF16 = native.NC_F32, native.NC_BF16
+A = 0x100000  # aligned fake device address (never dereferenced)
+
+
+def _gpu():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+@pytest.fixture(scope="module")
+def L():
+    return native.lib()
+
+
+def msg(L):
+    return L.nc_last_error_message().decode()
+
+
+def test_header_declares_exactly_the_exports():
+    with open(os.path.join(ROOT, "include", "ncattn.h")) as f:
+        src = f.read()
+    declared = set(re.findall(r"\b(nc_[a-z0-9_]+)\s*\(", src))
+    assert declared == set(native.EXPORTS)
+
+
+def test_library_exports_every_symbol(L):
+    for name in native.EXPORTS:
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", native.LIB_PATH], capture_output=True, text=True).stdout
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for name in native.EXPORTS:
+        assert name in syms, name
+
+
+def test_version_and_status_strings(L):
+    assert L.nc_abi_version() == 1
+    assert L.nc_status_string(0) == b"ok"
+    for s in range(1, 6):
+        assert L.nc_status_string(s) not in (b"ok", b"unknown status")
+    assert L.nc_status_string(99) == b"unknown status"
+
+
+def fwd(L, dt=BF16, B=1, T=64, H=2, Hkv=1, D=64, q=A, k=A, v=A, w=0, scale=0.125, out=A, lse=A):
+    return L.nc_attn_fwd(dt, B, T, H, Hkv, D, q, k, v, w, scale, out, lse, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(q=None), INVALID, "q is NULL"),
+    (dict(v=None), INVALID, "v is NULL"),
+    (dict(out=None), INVALID, "out"),
+    (dict(lse=None), INVALID, "lse"),
+    (dict(B=0), INVALID, "sizes"),
+    (dict(T=-1), INVALID, "sizes"),
+    (dict(H=3, Hkv=2), INVALID, "multiple"),
+    (dict(D=48), UNSUPPORTED, "head dim"),
+    (dict(D=256), UNSUPPORTED, "head dim"),
+    (dict(dt=7), INVALID, "dtype"),
+    (dict(k=A + 8), INVALID, "aligned"),
+    (dict(scale=0.0), INVALID, "scale"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(scale=float("inf")), INVALID, "scale"),
+    (dict(B=4096, T=4096, H=2, D=128), UNSUPPORTED, "exceeds"),
+])
+def test_fwd_validation(L, kw, code, needle):
+    assert fwd(L, **kw) == code
+    assert needle in msg(L)
+
+
+@pytest.mark.skipif(_gpu(), reason="with a GPU present a fully valid call would launch on fake pointers")
+def test_valid_call_without_gpu_reports_device(L):
+    assert fwd(L) == DEVICE
+    assert msg(L)
+
+
+def test_bwd_workspace_query_is_pure(L):
+    B, T, H, Hkv, D = 2, 100, 4, 2, 64
+    delta = -(-(B * H * T * 4) // 256) * 256
+    assert L.nc_attn_bwd_workspace_bytes(BF16, B, T, H, Hkv, D) == delta + B * T * H * D * 4
+    assert L.nc_attn_bwd_workspace_bytes(F32, B, T, H, Hkv, D) == delta
+    assert L.nc_attn_bwd_workspace_bytes(BF16, B, T, 3, 2, D) == 0
+    assert L.nc_attn_bwd_workspace_bytes(BF16, B, T, H, Hkv, 40) == 0
+
+
+def bwd(L, ws=A, wsb=1 << 30, dq=A, dout=A, dt=BF16, D=64, H=2, Hkv=1, w=0, scale=0.1):
+    return L.nc_attn_bwd(dt, 1, 64, H, Hkv, D, A, A, A, A, A, dout, w, scale, dq, A, A, ws, wsb, None)
+
+
+def test_bwd_validation(L):
+    assert bwd(L, dq=None) == INVALID
+    assert bwd(L, dout=A + 4) == INVALID
+    assert bwd(L, ws=None) == WORKSPACE
+    need = L.nc_attn_bwd_workspace_bytes(BF16, 1, 64, 2, 1, 64)
+    assert bwd(L, wsb=need - 1) == WORKSPACE
+    assert "workspace" in msg(L)
+    assert bwd(L, ws=A + 8) == WORKSPACE
+    assert bwd(L, D=96) == UNSUPPORTED
+    assert bwd(L, H=3, Hkv=2) == INVALID
+
+
+def test_decode_workspace_query_is_pure(L):
+    assert L.nc_attn_decode_workspace_bytes(BF16, 64, 10, 10, 128, 2048) == 64 * 10 * 8 * 130 * 4
+    assert L.nc_attn_decode_workspace_bytes(BF16, 3, 4, 2, 32, 257) == 3 * 4 * 2 * 34 * 4
+    assert L.nc_attn_decode_workspace_bytes(BF16, 3, 4, 3, 32, 257) == 0
+
+
+def dec(L, H=4, Hkv=2, D=64, T_max=100, seqlens=A, ws=A, wsb=1 << 30, lse=A, out=A, scale=0.1):
+    return L.nc_attn_decode(BF16, 2, H, Hkv, D, T_max, A, A, A, seqlens, 0, scale, out, lse, ws, wsb, None)
+
+
+def test_decode_validation(L):
+    assert dec(L, H=5, Hkv=1) == UNSUPPORTED  # group of 5 not built
+    assert "group" in msg(L)
+    assert dec(L, seqlens=None) == INVALID
+    assert dec(L, seqlens=A + 2) == INVALID
+    assert dec(L, lse=None) == INVALID
+    assert dec(L, out=A + 4) == INVALID
+    assert dec(L, ws=None) == WORKSPACE
+    assert dec(L, wsb=10) == WORKSPACE
+    assert dec(L, T_max=0) == INVALID
+    assert dec(L, scale=-1.0) == INVALID
+
+
+def test_rope_table_validation(L):
+    assert L.nc_rope_table(0, 64, 1e5, A, A, None) == INVALID
+    assert L.nc_rope_table(16, 63, 1e5, A, A, None) == INVALID
+    assert L.nc_rope_table(16, 64, 1.0, A, A, None) == INVALID
+    assert L.nc_rope_table(16, 64, 1e5, None, A, None) == INVALID
+    assert L.nc_rope_table(16, 64, 1e5, A + 2, A, None) == INVALID
+
+
+def test_prologue_validation(L):
+    f = L.nc_qk_prologue_fwd
+    assert f(BF16, 1, 64, 2, 1, 64, A, A, None, A, A, 32, 1e-6, A, A, None) == INVALID  # T > T_rope
+    assert "table" in msg(L)
+    assert f(BF16, 1, 16, 2, 1, 64, A, A, None, A, A, 32, -1.0, A, A, None) == INVALID  # eps
+    assert f(BF16, 1, 16, 2, 1, 64, A, A, A + 2, A, A, 32, 1e-6, A, A, None) == INVALID  # pos_offset
+    assert f(BF16, 1, 16, 2, 1, 64, A, A, None, A, A, 32, 1e-6, None, A, None) == INVALID
+    assert f(BF16, 1, 16, 2, 1, 80, A, A, None, A, A, 32, 1e-6, A, A, None) == UNSUPPORTED
+    g = L.nc_qk_prologue_bwd
+    assert g(BF16, 1, 16, 2, 1, 64, A, A, None, A, A, 32, 1e-6, None, A, A, A, None) == INVALID
+    assert g(BF16, 1, 16, 2, 1, 64, A, A, None, A, A, 32, 1e-6, A, A, A, None, None) == INVALID
+
+
+def test_error_message_is_per_thread(L):
+    import threading
+    assert fwd(L, q=None) == INVALID
+    seen = []
+
+    def other():
+        seen.append(msg(L))
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == [""]
+    assert "q is NULL" in msg(L)

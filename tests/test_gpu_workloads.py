@@ -1,0 +1,91 @@
+"""The five workloads at their full sizes, in the launch configuration the
+bench times, against the fp64 oracle on sampled batch rows (all heads, full
+length) or on whole tensors where the oracle is cheap."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import check, f64
+from transformer_attention_06_amd import synth
+from transformer_attention_06_amd.workload import FULL, workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def test_tiny_f32_end_to_end(gpu):
+    """Tiny fp32: prologue + attention forward and backward, both windows,
+    gradients w.r.t. the raw q and k, full tensors, max-abs <= 1e-4."""
+    from transformer_attention_06_amd import native
+    wl = workloads()["tiny_f32"]
+    B, T, H, Hkv, D = wl.B, wl.T, wl.H, wl.Hkv, wl.D
+    eps = 2.0 ** -23
+    q, k, v, do = (synth.normal_torch(s, 400 + i, "f32", "cuda") for i, s in
+                   enumerate([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D), (B, T, H, D)]))
+    c, s = native.nc_rope_table(10 * T, D)
+    pos = oracle.positions_from_offsets(B, T)
+    rqp, rkp = oracle.qk_prologue_fwd(f64(q), f64(k), pos, eps)
+    for w in wl.windows:
+        qp, kp = native.nc_qk_prologue_fwd(q, k, c, s, eps)
+        out, lse = native.nc_attn_fwd(qp, kp, v, w, wl.scale)
+        dqp, dkp, dv = native.nc_attn_bwd(qp, kp, v, out, lse, do, w, wl.scale)
+        dq, dk = native.nc_qk_prologue_bwd(q, k, c, s, eps, dqp, dkp)
+        ro, rl = oracle.attn_fwd(rqp, rkp, f64(v), w, wl.scale)
+        gqp, gkp, gv = oracle.attn_bwd(rqp, rkp, f64(v), f64(do), w, wl.scale)
+        gq, gk = oracle.qk_prologue_bwd(f64(q), f64(k), pos, gqp, gkp, eps)
+        check(f"tiny w{w} out", f64(out), ro, "f32", "out")
+        check(f"tiny w{w} lse", f64(lse), rl, "f32", "lse")
+        check(f"tiny w{w} dq", f64(dq), gq, "f32", "grad")
+        check(f"tiny w{w} dk", f64(dk), gk, "f32", "grad")
+        check(f"tiny w{w} dv", f64(dv), gv, "f32", "grad")
+
+
+def _sampled(native, wl, w, seed, rows):
+    import torch
+    B, T, H, Hkv, D = wl.B, wl.T, wl.H, wl.Hkv, wl.D
+    q = synth.normal_device((B, T, H, D), seed, "bf16")
+    k = synth.normal_device((B, T, Hkv, D), seed + 1, "bf16")
+    v = synth.normal_device((B, T, Hkv, D), seed + 2, "bf16")
+    do = synth.normal_device((B, T, H, D), seed + 3, "bf16")
+    out, lse = native.nc_attn_fwd(q, k, v, w, wl.scale)
+    dq, dk, dv = native.nc_attn_bwd(q, k, v, out, lse, do, w, wl.scale)
+    torch.cuda.synchronize()
+    sl = list(rows)
+    ro, rl = oracle.attn_fwd(f64(q[sl]), f64(k[sl]), f64(v[sl]), w, wl.scale)
+    gq, gk, gv = oracle.attn_bwd(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(do[sl]), w, wl.scale)
+    tag = f"{wl.name} w{w} rows{sl}"
+    check(tag + " out", f64(out[sl]), ro, "bf16", "out")
+    check(tag + " lse", f64(lse[sl]), rl, "bf16", "lse")
+    check(tag + " dq", f64(dq[sl]), gq, "bf16", "grad")
+    check(tag + " dk", f64(dk[sl]), gk, "bf16", "grad")
+    check(tag + " dv", f64(dv[sl]), gv, "bf16", "grad")
+
+
+@pytest.mark.parametrize("name,w", [("d20_bf16", 1024), ("d20_bf16", FULL), ("d12_bf16", 1024),
+                                    ("gqa_bf16", FULL), ("gqa_bf16", 1024)])
+def test_full_size_sampled_rows(gpu, name, w):
+    from transformer_attention_06_amd import native
+    wl = workloads()[name]
+    rng = np.random.default_rng(500)
+    rows = sorted(set([0, wl.B - 1] + [int(rng.integers(0, wl.B))]))[:2]
+    print("workload", name, "window", w, "rows", rows, flush=True)
+    _sampled(native, wl, w, 600 + w, rows)
+
+
+def test_decode_full_size(gpu):
+    import torch
+    from transformer_attention_06_amd import native
+    wl = workloads()["decode_bf16"]
+    B, H, Hkv, D, T_max = wl.B, wl.H, wl.Hkv, wl.D, wl.T
+    lens = synth.seqlens_np(B, T_max, 700)
+    sl = torch.from_numpy(lens).cuda()
+    for w in (1024, FULL):
+        q = synth.normal_device((B, H, D), 701, "bf16")
+        kc = synth.normal_device((B, T_max, Hkv, D), 702, "bf16")
+        vc = synth.normal_device((B, T_max, Hkv, D), 703, "bf16")
+        out, lse = native.nc_attn_decode(q, kc, vc, sl, w, wl.scale)
+        ro, rl = oracle.decode(f64(q), f64(kc), f64(vc), lens, w, wl.scale)
+        check(f"decode w{w} out", f64(out), ro, "bf16", "out")
+        check(f"decode w{w} lse", f64(lse), rl, "bf16", "lse")

@@ -1,0 +1,270 @@
+// libncattn C ABI: argument validation and dispatch. Every entry point
+// checks its arguments before any HIP call, then checks that the current
+// device is a gfx950, enqueues its kernels on the caller's stream and
+// returns without synchronising.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+
+#include "../../include/ncattn.h"
+#include "kernels.hpp"
+
+namespace nc {
+bool decode_group_supported(int G);
+}
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+nc_status fail(nc_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof g_msg, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+constexpr long long kMaxElems = 2147483647LL;  // per-tensor element count limit (int32 indexing margin)
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Common shape checks of the attention entry points.
+nc_status check_shape(nc_dtype dt, int B, int T, int H, int Hkv, int D) {
+  if (dt != NC_F32 && dt != NC_BF16) return fail(NC_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+  if (B < 1 || T < 1 || H < 1 || Hkv < 1 || D < 1)
+    return fail(NC_ERR_INVALID_ARG, "sizes must be >= 1 (B=%d T=%d H=%d Hkv=%d D=%d)", B, T, H, Hkv, D);
+  if (H % Hkv != 0) return fail(NC_ERR_INVALID_ARG, "H=%d is not a multiple of Hkv=%d", H, Hkv);
+  if (D != 32 && D != 64 && D != 128) return fail(NC_ERR_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", D);
+  if ((long long)B * T * H * D > kMaxElems)
+    return fail(NC_ERR_UNSUPPORTED, "tensor of B*T*H*D=%lld elements exceeds 2^31-1", (long long)B * T * H * D);
+  return NC_OK;
+}
+
+nc_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(NC_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(NC_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return NC_OK;
+}
+
+nc_status check_scale(float scale) {
+  if (!(scale > 0.f) || !isfinite(scale)) return fail(NC_ERR_INVALID_ARG, "scale must be finite and > 0");
+  return NC_OK;
+}
+
+// The current device must be a gfx950. Properties are cached per device id.
+nc_status check_device(int* dev_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(NC_ERR_DEVICE, "no HIP device available");
+  }
+  static std::mutex mu;
+  static int known[64];  // 0 unknown, 1 gfx950, 2 other
+  if (dev >= 64) return fail(NC_ERR_DEVICE, "device id %d out of range", dev);
+  int state;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    state = known[dev];
+  }
+  if (state == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(NC_ERR_DEVICE, "cannot query device %d", dev);
+    }
+    state = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    std::lock_guard<std::mutex> lk(mu);
+    known[dev] = state;
+  }
+  if (state != 1) return fail(NC_ERR_DEVICE, "device %d is not a gfx950", dev);
+  if (dev_out) *dev_out = dev;
+  return NC_OK;
+}
+
+nc_status finish(hipError_t e, hipStream_t s, const char* what) {
+  if (e != hipSuccess) return fail(NC_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  static const bool debug_sync = getenv("NC_DEBUG_SYNC") && getenv("NC_DEBUG_SYNC")[0] == '1';
+  if (debug_sync) {
+    e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(NC_ERR_LAUNCH, "%s: kernel failed: %s", what, hipGetErrorString(e));
+  }
+  g_msg[0] = 0;
+  return NC_OK;
+}
+
+#define NC_TRY(x)                \
+  do {                           \
+    nc_status _st = (x);         \
+    if (_st != NC_OK) return _st; \
+  } while (0)
+
+int norm_window(int window, int T) { return (window <= 0 || window >= T) ? 0 : window; }
+
+int decode_splits(int T_max) { return (T_max + nc::kDecodeSplit - 1) / nc::kDecodeSplit; }
+
+}  // namespace
+
+extern "C" {
+
+int nc_abi_version(void) { return NCATTN_ABI_VERSION; }
+
+const char* nc_status_string(nc_status s) {
+  switch (s) {
+    case NC_OK: return "ok";
+    case NC_ERR_INVALID_ARG: return "invalid argument";
+    case NC_ERR_UNSUPPORTED: return "unsupported";
+    case NC_ERR_WORKSPACE: return "workspace too small";
+    case NC_ERR_DEVICE: return "no usable gfx950 device";
+    case NC_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* nc_last_error_message(void) { return g_msg; }
+
+nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
+                      const void* v, int window, float scale, void* out, float* lse, nc_stream stream) {
+  NC_TRY(check_shape(dt, B, T, H, Hkv, D));
+  NC_TRY(check_ptr(q, "q"));
+  NC_TRY(check_ptr(k, "k"));
+  NC_TRY(check_ptr(v, "v"));
+  NC_TRY(check_ptr(out, "out"));
+  NC_TRY(check_ptr(lse, "lse"));
+  NC_TRY(check_scale(scale));
+  NC_TRY(check_device(nullptr));
+  nc::FwdParams p{q, k, v, out, lse, B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f};
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dt == NC_BF16 ? nc::launch_attn_fwd_bf16(p, s) : nc::launch_attn_fwd_f32(p, s), s, "nc_attn_fwd");
+}
+
+size_t nc_attn_bwd_workspace_bytes(nc_dtype dt, int B, int T, int H, int Hkv, int D) {
+  if (check_shape(dt, B, T, H, Hkv, D) != NC_OK) return 0;
+  size_t delta = (size_t)B * H * T * 4;
+  delta = (delta + 255) & ~(size_t)255;
+  const size_t acc = dt == NC_BF16 ? (size_t)B * T * H * D * 4 : 0;
+  return delta + acc;
+}
+
+nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
+                      const void* v, const void* out, const float* lse, const void* dout, int window,
+                      float scale, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                      nc_stream stream) {
+  NC_TRY(check_shape(dt, B, T, H, Hkv, D));
+  NC_TRY(check_ptr(q, "q"));
+  NC_TRY(check_ptr(k, "k"));
+  NC_TRY(check_ptr(v, "v"));
+  NC_TRY(check_ptr(out, "out"));
+  NC_TRY(check_ptr(lse, "lse"));
+  NC_TRY(check_ptr(dout, "dout"));
+  NC_TRY(check_ptr(dq, "dq"));
+  NC_TRY(check_ptr(dk, "dk"));
+  NC_TRY(check_ptr(dv, "dv"));
+  NC_TRY(check_scale(scale));
+  const size_t need = nc_attn_bwd_workspace_bytes(dt, B, T, H, Hkv, D);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+    return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  NC_TRY(check_device(nullptr));
+  size_t delta_bytes = ((size_t)B * H * T * 4 + 255) & ~(size_t)255;
+  nc::BwdParams p{q, k, v, out, lse, dout, dq, dk, dv, (float*)workspace,
+                  dt == NC_BF16 ? (float*)((char*)workspace + delta_bytes) : nullptr,
+                  B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f};
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dt == NC_BF16 ? nc::launch_attn_bwd_bf16(p, s) : nc::launch_attn_bwd_f32(p, s), s, "nc_attn_bwd");
+}
+
+size_t nc_attn_decode_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, int D, int T_max) {
+  if (check_shape(dt, B, T_max, H, Hkv, D) != NC_OK) return 0;
+  return (size_t)B * H * decode_splits(T_max) * (D + 2) * 4;
+}
+
+nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q,
+                         const void* k_cache, const void* v_cache, const int32_t* seqlens, int window,
+                         float scale, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                         nc_stream stream) {
+  NC_TRY(check_shape(dt, B, T_max, H, Hkv, D));
+  if ((long long)B * T_max * Hkv * D > kMaxElems)
+    return fail(NC_ERR_UNSUPPORTED, "cache of B*T_max*Hkv*D elements exceeds 2^31-1");
+  if (!nc::decode_group_supported(H / Hkv))
+    return fail(NC_ERR_UNSUPPORTED, "decode supports query groups H/Hkv in {1,2,3,4,6,8}, got %d", H / Hkv);
+  NC_TRY(check_ptr(q, "q"));
+  NC_TRY(check_ptr(k_cache, "k_cache"));
+  NC_TRY(check_ptr(v_cache, "v_cache"));
+  if (!seqlens) return fail(NC_ERR_INVALID_ARG, "seqlens is NULL");
+  if (((uintptr_t)seqlens & 3u) != 0) return fail(NC_ERR_INVALID_ARG, "seqlens is not 4-byte aligned");
+  NC_TRY(check_ptr(out, "out"));
+  if (!lse) return fail(NC_ERR_INVALID_ARG, "lse is NULL");
+  if (((uintptr_t)lse & 3u) != 0) return fail(NC_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  NC_TRY(check_scale(scale));
+  const size_t need = nc_attn_decode_workspace_bytes(dt, B, H, Hkv, D, T_max);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+    return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  NC_TRY(check_device(nullptr));
+  nc::DecodeParams p{q, k_cache, v_cache, seqlens, out, lse, (float*)workspace, B, H, Hkv, D, T_max,
+                     window <= 0 ? 0 : window, decode_splits(T_max), scale, scale * 1.4426950408889634f};
+  hipStream_t s = (hipStream_t)stream;
+  return finish(nc::launch_decode(p, dt == NC_BF16, s), s, "nc_attn_decode");
+}
+
+nc_status nc_rope_table(int T_rope, int D, double base, float* cos_out, float* sin_out, nc_stream stream) {
+  if (T_rope < 1) return fail(NC_ERR_INVALID_ARG, "T_rope must be >= 1");
+  if (D < 2 || D > 256 || (D & 1)) return fail(NC_ERR_INVALID_ARG, "D must be even, 2..256");
+  if (!(base > 1.0) || !isfinite(base)) return fail(NC_ERR_INVALID_ARG, "base must be finite and > 1");
+  if ((long long)T_rope * (D / 2) > kMaxElems) return fail(NC_ERR_UNSUPPORTED, "table too large");
+  if (!cos_out || !sin_out) return fail(NC_ERR_INVALID_ARG, "table pointer is NULL");
+  if (((uintptr_t)cos_out & 3u) || ((uintptr_t)sin_out & 3u))
+    return fail(NC_ERR_INVALID_ARG, "table pointers must be 4-byte aligned");
+  NC_TRY(check_device(nullptr));
+  hipStream_t s = (hipStream_t)stream;
+  return finish(nc::launch_rope_table(T_rope, D, base, cos_out, sin_out, s), s, "nc_rope_table");
+}
+
+static nc_status prologue_common(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
+                                 const int32_t* pos_offset, const float* cos_tab, const float* sin_tab,
+                                 int T_rope, float eps) {
+  NC_TRY(check_shape(dt, B, T, H, Hkv, D));
+  NC_TRY(check_ptr(q, "q"));
+  NC_TRY(check_ptr(k, "k"));
+  NC_TRY(check_ptr(cos_tab, "cos"));
+  NC_TRY(check_ptr(sin_tab, "sin"));
+  if (pos_offset && ((uintptr_t)pos_offset & 3u)) return fail(NC_ERR_INVALID_ARG, "pos_offset is not 4-byte aligned");
+  if (T_rope < 1) return fail(NC_ERR_INVALID_ARG, "T_rope must be >= 1");
+  if (!pos_offset && T > T_rope) return fail(NC_ERR_INVALID_ARG, "T=%d exceeds the table length %d", T, T_rope);
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(NC_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return NC_OK;
+}
+
+nc_status nc_qk_prologue_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
+                             const int32_t* pos_offset, const float* cos_tab, const float* sin_tab, int T_rope,
+                             float eps, void* q_out, void* k_out, nc_stream stream) {
+  NC_TRY(prologue_common(dt, B, T, H, Hkv, D, q, k, pos_offset, cos_tab, sin_tab, T_rope, eps));
+  NC_TRY(check_ptr(q_out, "q_out"));
+  NC_TRY(check_ptr(k_out, "k_out"));
+  NC_TRY(check_device(nullptr));
+  nc::PrologueParams p{q, k, pos_offset, cos_tab, sin_tab, nullptr, nullptr, q_out, k_out, B, T, H, Hkv, D, T_rope, eps};
+  hipStream_t s = (hipStream_t)stream;
+  return finish(nc::launch_prologue(p, dt == NC_BF16, false, s), s, "nc_qk_prologue_fwd");
+}
+
+nc_status nc_qk_prologue_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
+                             const int32_t* pos_offset, const float* cos_tab, const float* sin_tab, int T_rope,
+                             float eps, const void* dq_out, const void* dk_out, void* dq, void* dk,
+                             nc_stream stream) {
+  NC_TRY(prologue_common(dt, B, T, H, Hkv, D, q, k, pos_offset, cos_tab, sin_tab, T_rope, eps));
+  NC_TRY(check_ptr(dq_out, "dq_out"));
+  NC_TRY(check_ptr(dk_out, "dk_out"));
+  NC_TRY(check_ptr(dq, "dq"));
+  NC_TRY(check_ptr(dk, "dk"));
+  NC_TRY(check_device(nullptr));
+  nc::PrologueParams p{q, k, pos_offset, cos_tab, sin_tab, dq_out, dk_out, dq, dk, B, T, H, Hkv, D, T_rope, eps};
+  hipStream_t s = (hipStream_t)stream;
+  return finish(nc::launch_prologue(p, dt == NC_BF16, true, s), s, "nc_qk_prologue_bwd");
+}
+
+}  // extern "C"

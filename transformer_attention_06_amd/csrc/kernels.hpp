@@ -1,0 +1,80 @@
+// Kernel parameter blocks and launchers (internal to libncattn).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nc {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  int B, T, H, Hkv, D;
+  int window;        // 0 = full causal, otherwise 1 <= window < T
+  float scale;       // logit scale
+  float scale_log2;  // scale * log2(e)
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;   // [B, H, T] workspace
+  float* dq_acc;  // [B, T, H, D] workspace
+  int B, T, H, Hkv, D;
+  int window;
+  float scale;
+  float scale_log2;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* seqlens;
+  void* out;
+  float* lse;
+  float* part;  // [B, H, n_split, D + 2] workspace (acc[D], m, l)
+  int B, H, Hkv, D, T_max;
+  int window;  // <= 0 full
+  int n_split;
+  float scale;
+  float scale_log2;
+};
+
+struct PrologueParams {
+  const void* q;
+  const void* k;
+  const int32_t* pos_offset;
+  const float* cos_tab;
+  const float* sin_tab;
+  const void* dq_out;  // backward only
+  const void* dk_out;  // backward only
+  void* q_out;         // forward: q'; backward: dq
+  void* k_out;         // forward: k'; backward: dk
+  int B, T, H, Hkv, D, T_rope;
+  float eps;
+};
+
+// Decode split size in keys (one workgroup per (b, kv head, split)).
+constexpr int kDecodeSplit = 256;
+
+hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s);
+hipError_t launch_attn_fwd_f32(const FwdParams& p, hipStream_t s);
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s);
+hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t s);
+hipError_t launch_rope_table(int T_rope, int D, double base, float* c, float* sn, hipStream_t s);
+hipError_t launch_prologue(const PrologueParams& p, bool bf16, bool backward, hipStream_t s);
+
+}  // namespace nc

@@ -1,0 +1,249 @@
+"""ctypes binding of libncattn.so (argument marshalling only).
+
+The functions below carry the names of the C entry points declared in
+include/ncattn.h. They take torch tensors for device memory and the current
+torch stream, pass raw pointers and sizes to the library, and raise
+``NcError`` on a non-zero status. Every step of the computation runs in the
+library's HIP kernels; there is no fallback: if the library is missing or
+cannot be loaded, the first call raises.
+"""
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("NCATTN_LIB") or os.path.join(HERE, "libncattn.so")
+
+NC_F32, NC_BF16 = 0, 1
+STATUS = {0: "NC_OK", 1: "NC_ERR_INVALID_ARG", 2: "NC_ERR_UNSUPPORTED", 3: "NC_ERR_WORKSPACE",
+          4: "NC_ERR_DEVICE", 5: "NC_ERR_LAUNCH"}
+
+# every symbol include/ncattn.h declares
+EXPORTS = (
+    "nc_abi_version", "nc_status_string", "nc_last_error_message",
+    "nc_attn_fwd", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd",
+    "nc_attn_decode_workspace_bytes", "nc_attn_decode",
+    "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd",
+)
+
+
+class NcError(RuntimeError):
+    def __init__(self, name, status, msg):
+        super().__init__(f"{name}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+_i, _p, _f, _d, _sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_float, ctypes.c_double, ctypes.c_size_t
+
+_SIGS = {
+    "nc_abi_version": ([], _i),
+    "nc_status_string": ([_i], ctypes.c_char_p),
+    "nc_last_error_message": ([], ctypes.c_char_p),
+    "nc_attn_fwd": ([_i] * 6 + [_p, _p, _p, _i, _f, _p, _p, _p], _i),
+    "nc_attn_bwd_workspace_bytes": ([_i] * 6, _sz),
+    "nc_attn_bwd": ([_i] * 6 + [_p] * 6 + [_i, _f] + [_p] * 3 + [_p, _sz, _p], _i),
+    "nc_attn_decode_workspace_bytes": ([_i] * 6, _sz),
+    "nc_attn_decode": ([_i] * 6 + [_p] * 4 + [_i, _f, _p, _p, _p, _sz, _p], _i),
+    "nc_rope_table": ([_i, _i, _d, _p, _p, _p], _i),
+    "nc_qk_prologue_fwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p], _i),
+    "nc_qk_prologue_bwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p, _p, _p], _i),
+}
+
+
+def lib():
+    """Load libncattn.so once and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise OSError(f"{LIB_PATH} not found: build it with "
+                              "`python -m transformer_attention_06_amd.build`")
+            L = ctypes.CDLL(LIB_PATH)
+            for name, (args, res) in _SIGS.items():
+                fn = getattr(L, name)
+                fn.argtypes = args
+                fn.restype = res
+            _lib = L
+        return _lib
+
+
+def _raise_on(name, status):
+    if status != 0:
+        raise NcError(name, status, lib().nc_last_error_message().decode())
+
+
+def _dt(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return NC_BF16
+    if t.dtype == torch.float32:
+        return NC_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libncattn must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _empty(shape, like, dtype=None):
+    import torch
+    return torch.empty(shape, dtype=dtype or like.dtype, device=like.device)
+
+
+# ----------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+
+
+def nc_abi_version():
+    return lib().nc_abi_version()
+
+
+def nc_attn_fwd(q, k, v, window, scale, out=None, lse=None, stream=None):
+    """q [B,T,H,D], k/v [B,T,Hkv,D] -> (out [B,T,H,D], lse [B,H,T] float32)."""
+    import torch
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    out = _empty(q.shape, q) if out is None else out
+    lse = _empty((B, H, T), q, torch.float32) if lse is None else lse
+    st = lib().nc_attn_fwd(_dt(q), B, T, H, Hkv, D, _ptr(q), _ptr(k), _ptr(v), int(window),
+                           float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _raise_on("nc_attn_fwd", st)
+    return out, lse
+
+
+def nc_attn_bwd_workspace_bytes(dtype_code, B, T, H, Hkv, D):
+    return lib().nc_attn_bwd_workspace_bytes(dtype_code, B, T, H, Hkv, D)
+
+
+def nc_attn_bwd(q, k, v, out, lse, dout, window, scale, dq=None, dk=None, dv=None,
+                workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of sum(out * dout); dk/dv summed over each query group."""
+    import torch
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    dq = _empty(q.shape, q) if dq is None else dq
+    dk = _empty(k.shape, k) if dk is None else dk
+    dv = _empty(v.shape, v) if dv is None else dv
+    need = nc_attn_bwd_workspace_bytes(_dt(q), B, T, H, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().nc_attn_bwd(_dt(q), B, T, H, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                           _ptr(dout), int(window), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise_on("nc_attn_bwd", st)
+    return dq, dk, dv
+
+
+def nc_attn_decode_workspace_bytes(dtype_code, B, H, Hkv, D, T_max):
+    return lib().nc_attn_decode_workspace_bytes(dtype_code, B, H, Hkv, D, T_max)
+
+
+def nc_attn_decode(q, k_cache, v_cache, seqlens, window, scale, out=None, lse=None,
+                   workspace=None, stream=None):
+    """q [B,H,D], caches [B,T_max,Hkv,D], seqlens int32 [B] (device) -> (out [B,H,D], lse [B,H])."""
+    import torch
+    B, H, D = q.shape
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if seqlens.dtype != torch.int32:
+        raise TypeError("seqlens must be int32")
+    out = _empty(q.shape, q) if out is None else out
+    lse = _empty((B, H), q, torch.float32) if lse is None else lse
+    need = nc_attn_decode_workspace_bytes(_dt(q), B, H, Hkv, D, T_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().nc_attn_decode(_dt(q), B, H, Hkv, D, T_max, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                              _ptr(seqlens), int(window), float(scale), _ptr(out), _ptr(lse),
+                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream))
+    _raise_on("nc_attn_decode", st)
+    return out, lse
+
+
+def nc_rope_table(T_rope, D, base=100000.0, device="cuda", stream=None):
+    """cos, sin float32 [T_rope, D/2] built on the device in float64."""
+    import torch
+    c = torch.empty((T_rope, D // 2), dtype=torch.float32, device=device)
+    s = torch.empty((T_rope, D // 2), dtype=torch.float32, device=device)
+    st = lib().nc_rope_table(int(T_rope), int(D), float(base), _ptr(c), _ptr(s), _stream(stream))
+    _raise_on("nc_rope_table", st)
+    return c, s
+
+
+def nc_qk_prologue_fwd(q, k, cos, sin, eps, pos_offset=None, q_out=None, k_out=None, stream=None):
+    """(RoPE(RMSNorm(q)), RoPE(RMSNorm(k))) at positions pos_offset[b] + t."""
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    q_out = _empty(q.shape, q) if q_out is None else q_out
+    k_out = _empty(k.shape, k) if k_out is None else k_out
+    st = lib().nc_qk_prologue_fwd(_dt(q), B, T, H, Hkv, D, _ptr(q), _ptr(k), _ptr(pos_offset),
+                                  _ptr(cos), _ptr(sin), cos.shape[0], float(eps), _ptr(q_out),
+                                  _ptr(k_out), _stream(stream))
+    _raise_on("nc_qk_prologue_fwd", st)
+    return q_out, k_out
+
+
+def nc_qk_prologue_bwd(q, k, cos, sin, eps, dq_out, dk_out, pos_offset=None, dq=None, dk=None,
+                       stream=None):
+    """Gradients w.r.t. raw q, k from gradients w.r.t. the prologue outputs."""
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    dq = _empty(q.shape, q) if dq is None else dq
+    dk = _empty(k.shape, k) if dk is None else dk
+    st = lib().nc_qk_prologue_bwd(_dt(q), B, T, H, Hkv, D, _ptr(q), _ptr(k), _ptr(pos_offset),
+                                  _ptr(cos), _ptr(sin), cos.shape[0], float(eps), _ptr(dq_out),
+                                  _ptr(dk_out), _ptr(dq), _ptr(dk), _stream(stream))
+    _raise_on("nc_qk_prologue_bwd", st)
+    return dq, dk
+
+
+# ----------------------------------------------------------------------------
+# autograd wrapper: saves out and lse, recomputes P in the backward kernel
+
+def attention(q, k, v, window, scale):
+    return _Attention.apply(q, k, v, window, scale)
+
+
+def _make_fn():
+    import torch
+
+    class Attention(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, window, scale):
+            out, lse = nc_attn_fwd(q, k, v, window, scale)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.window, ctx.scale = window, scale
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse = ctx.saved_tensors
+            dq, dk, dv = nc_attn_bwd(q, k, v, out, lse, dout.contiguous(), ctx.window, ctx.scale)
+            return dq, dk, dv, None, None
+
+    return Attention
+
+
+class _Lazy:
+    _fn = None
+
+    def apply(self, *a):
+        if _Lazy._fn is None:
+            _Lazy._fn = _make_fn()
+        return _Lazy._fn.apply(*a)
+
+
+_Attention = _Lazy()
