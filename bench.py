@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""Throughput of the nanochat attention hot path on one MI355X.
+
+One step = one pass of the training-side hot path over one batch of the
+d20-shaped workload (B=32, T=2048, H=Hkv=10, D=128, bf16, 20 layers in the
+SSSL window schedule: 15 layers with a 1024-key window, 5 full causal):
+for every layer the QK prologue (RMSNorm + RoPE) forward and attention
+forward, then, in reverse layer order, attention backward and prologue
+backward. The reported value is band-counted attention fwd+bwd FLOPs
+(12 * D per visible query/key pair, per (b, h)) divided by the step time, so
+the prologue's time counts against it. The decode workload (64 rows, one
+query each, cache lengths uniform on 1..2048, same 20-layer schedule) is
+timed as a separate phase and reported in GB/s of algorithmic bytes.
+
+Inputs are seeded N(0, 1) bf16 tensors drawn on the device and resident in
+HBM before the timed region. Prints one JSON line on stdout; progress goes
+to stderr.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "attn fwd+bwd TFLOP/s (band-counted) at d20 T=2048; decode GB/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+class Timer:
+    """Pairs of torch.cuda events on the current stream, summed per label."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def pair(self, label):
+        t = self.torch
+        b, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        self.pairs.setdefault(label, []).append((b, e))
+        return b, e
+
+    def totals(self):
+        return {k: (sum(b.elapsed_time(e) for b, e in v), len(v)) for k, v in self.pairs.items()}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(attention shards by batch row or GQA group with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from transformer_attention_06_amd import native, synth
+    from transformer_attention_06_amd.workload import (FULL, attn_flops, band_pairs, decode_bytes,
+                                                       workloads)
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    native.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    wl = workloads()["d20_bf16"]
+    B, T, H, Hkv, D = wl.B, wl.T, wl.H, wl.Hkv, wl.D
+    L = len(wl.windows)
+    scale, eps = wl.scale, 2.0 ** -23
+    log(f"allocating d20 inputs: {L} layers x q,k,v,dout [{B},{T},{H},{D}] bf16")
+    qr = [synth.normal_device((B, T, H, D), 1000 + 10 * l, "bf16") for l in range(L)]
+    kr = [synth.normal_device((B, T, Hkv, D), 1001 + 10 * l, "bf16") for l in range(L)]
+    vv = [synth.normal_device((B, T, Hkv, D), 1002 + 10 * l, "bf16") for l in range(L)]
+    do = [synth.normal_device((B, T, H, D), 1003 + 10 * l, "bf16") for l in range(L)]
+    qp = [torch.empty_like(x) for x in qr]
+    kp = [torch.empty_like(x) for x in kr]
+    out = [torch.empty_like(x) for x in qr]
+    lse = [torch.empty((B, H, T), dtype=torch.float32, device=dev) for _ in range(L)]
+    dqp, dkp, dv = torch.empty_like(qr[0]), torch.empty_like(kr[0]), torch.empty_like(vv[0])
+    dq, dk = torch.empty_like(qr[0]), torch.empty_like(kr[0])
+    ws = torch.empty(native.nc_attn_bwd_workspace_bytes(native.NC_BF16, B, T, H, Hkv, D),
+                     dtype=torch.uint8, device=dev)
+    cos, sin = native.nc_rope_table(10 * T, D, 100000.0)
+
+    def step(tm=None):
+        def ev(label):
+            return tm.pair(label) if tm else (None, None)
+
+        for l in range(L):
+            b, e = ev("prologue_fwd")
+            b and b.record()
+            native.nc_qk_prologue_fwd(qr[l], kr[l], cos, sin, eps, q_out=qp[l], k_out=kp[l])
+            e and e.record()
+            b, e = ev("attn_fwd")
+            b and b.record()
+            native.nc_attn_fwd(qp[l], kp[l], vv[l], wl.windows[l], scale, out=out[l], lse=lse[l])
+            e and e.record()
+        for l in reversed(range(L)):
+            b, e = ev("attn_bwd")
+            if tm:
+                mb, me = tm.pair("attn_bwd_main")
+                mb.record()  # materialise the events before handing them to the library
+                me.record()
+                native.nc_profile_bwd_main(mb, me)
+            b and b.record()
+            native.nc_attn_bwd(qp[l], kp[l], vv[l], out[l], lse[l], do[l], wl.windows[l], scale,
+                               dq=dqp, dk=dkp, dv=dv, workspace=ws)
+            e and e.record()
+            if tm:
+                native.nc_profile_bwd_main()
+            b, e = ev("prologue_bwd")
+            b and b.record()
+            native.nc_qk_prologue_bwd(qr[l], kr[l], cos, sin, eps, dqp, dkp, dq=dq, dk=dk)
+            e and e.record()
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # whole-step timing: nothing but the work between the two events
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+    # per-kernel timing in a second pass of the same steps (events between launches)
+    tm = Timer(torch)
+    for _ in range(args.steps):
+        step(tm)
+    torch.cuda.synchronize()
+    tot = tm.totals()
+    flops_f = attn_flops(B, T, H, D, wl.windows, "fwd")
+    flops_b = attn_flops(B, T, H, D, wl.windows, "bwd")
+    value = (flops_f + flops_b) / (ms_step * 1e-3) / 1e12
+    kern = {}
+    for label, (ms, n) in tot.items():
+        per_step = ms / args.steps
+        row = {"ms_per_step": round(per_step, 4), "launches_per_step": n // args.steps,
+               "avg_ms_per_launch": round(ms / n, 5)}
+        if label in ("attn_fwd",):
+            row["tflops"] = round(flops_f / (per_step * 1e-3) / 1e12, 2)
+            row["frac_bf16_peak"] = round(row["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if label in ("attn_bwd", "attn_bwd_main"):
+            row["tflops"] = round(flops_b / (per_step * 1e-3) / 1e12, 2)
+            row["frac_bf16_peak"] = round(row["tflops"] / PEAK_BF16_TFLOPS, 4)
+        if label.startswith("prologue"):
+            nbytes = 2 * L * (B * T * (H + Hkv) * D * 2) * (1 if label.endswith("fwd") else 1.5)
+            row["gbs"] = round(nbytes / (per_step * 1e-3) / 1e9, 1)
+        kern[label] = row
+    log("kernels:", json.dumps(kern))
+
+    # ---------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        dw = workloads()["decode_bf16"]
+        DB, DH, DHkv, DD, Tm = dw.B, dw.H, dw.Hkv, dw.D, dw.T
+        lens = synth.seqlens_np(DB, Tm, 2000)
+        sl = torch.from_numpy(lens).to(dev)
+        log(f"allocating decode caches: {len(dw.windows)} layers x [{DB},{Tm},{DHkv},{DD}] bf16 x2")
+        dq_ = [synth.normal_device((DB, DH, DD), 2001 + 10 * l, "bf16") for l in range(len(dw.windows))]
+        kc = [synth.normal_device((DB, Tm, DHkv, DD), 2002 + 10 * l, "bf16") for l in range(len(dw.windows))]
+        vc = [synth.normal_device((DB, Tm, DHkv, DD), 2003 + 10 * l, "bf16") for l in range(len(dw.windows))]
+        dout_ = torch.empty_like(dq_[0])
+        dlse = torch.empty((DB, DH), dtype=torch.float32, device=dev)
+        dws = torch.empty(native.nc_attn_decode_workspace_bytes(native.NC_BF16, DB, DH, DHkv, DD, Tm),
+                          dtype=torch.uint8, device=dev)
+
+        def dstep():
+            for l, w in enumerate(dw.windows):
+                native.nc_attn_decode(dq_[l], kc[l], vc[l], sl, w, dw.scale, out=dout_, lse=dlse,
+                                      workspace=dws)
+
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            dstep()
+        t1.record()
+        torch.cuda.synchronize()
+        dms = t0.elapsed_time(t1) / args.steps
+        nbytes = sum(decode_bytes(lens, DH, DHkv, DD, w) for w in dw.windows)
+        gbs = nbytes / (dms * 1e-3) / 1e9
+        decode = {"workload": "decode_bf16: 64 rows x 1 query, H=Hkv=10, D=128, cache lengths "
+                              "uniform 1..2048, 20-layer SSSL step (15 x w=1024, 5 full)",
+                  "ms_per_step": round(dms, 4), "bytes_per_step": nbytes, "gbs": round(gbs, 1),
+                  "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+        log("decode:", json.dumps(decode))
+        del kc, vc
+
+    # ------------------------------------------------------------- roofline
+    dom = max(("attn_fwd", "attn_bwd_main"), key=lambda k: kern[k]["ms_per_step"])
+    dom_flops = flops_f if dom == "attn_fwd" else flops_b
+    n_launch = kern[dom]["launches_per_step"]
+    achieved = dom_flops / n_launch / (kern[dom]["avg_ms_per_launch"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None,
+                "note": "achieved = band-counted flops per launch (8*D or 4*D per visible pair, "
+                        "B*H*pairs(T,w) pairs) / average launch time, averaged over the 20 layers"}
+
+    # --------------------------------------------------------- cpu baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, np, torch, synth, wl, qr, kr, vv, do, cos, eps, band_pairs, FULL)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, drawn on the device)",
+        "config": {"workload": "d20_bf16: B=32 T=2048 H=Hkv=10 D=128, 20 layers SSSL "
+                               "(15 x window 1024, 5 full causal); step = prologue fwd + attention fwd "
+                               "per layer, then attention bwd + prologue bwd per layer",
+                   "B": B, "T": T, "H": H, "Hkv": Hkv, "D": D, "windows": wl.windows,
+                   "band_flops_fwd": flops_f, "band_flops_bwd": flops_b},
+        "attn_only_tflops": round((flops_f + flops_b) /
+                                  ((kern["attn_fwd"]["ms_per_step"] + kern["attn_bwd"]["ms_per_step"]) * 1e-3)
+                                  / 1e12, 2),
+        "kernels": kern,
+        "decode": decode,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(args, np, torch, synth, wl, qr, kr, vv, do, cos, eps, band_pairs, FULL):
+    """The fp64 oracle, as it stands, on a bounded sample of the same inputs:
+    whole batch rows (all heads) of one windowed layer and one full layer,
+    prologue + attention forward + backward, alternating until the budget is
+    spent. Rate in band-counted TFLOP/s like the GPU value."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    layers = [wl.windows.index(1024), wl.windows.index(FULL)]
+    T, H, D = wl.T, wl.H, wl.D
+    pos = oracle.positions_from_offsets(1, T)
+    done_flops, n_rows, elapsed = 0, 0, 0.0
+    b = 0
+    while elapsed < args.cpu_seconds and b < wl.B:
+        for l in layers:
+            w = wl.windows[l]
+            q = synth.to_f64(qr[l][b:b + 1])
+            k = synth.to_f64(kr[l][b:b + 1])
+            v = synth.to_f64(vv[l][b:b + 1])
+            g = synth.to_f64(do[l][b:b + 1])
+            t = time.perf_counter()
+            q1, k1 = oracle.qk_prologue_fwd(q, k, pos, eps)
+            oracle.attn_fwd(q1, k1, v, w, wl.scale)
+            gq, gk, _ = oracle.attn_bwd(q1, k1, v, g, w, wl.scale)
+            oracle.qk_prologue_bwd(q, k, pos, gq, gk, eps)
+            elapsed += time.perf_counter() - t
+            done_flops += 12 * D * H * band_pairs(T, w)
+            n_rows += 1
+        b += 1
+        log(f"cpu baseline: {n_rows} row-layers in {elapsed:.1f} s")
+    return {"value": round(done_flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_rows} (batch row, layer) pairs of d20 (all 10 heads, T=2048; layers with "
+                      f"window 1024 and full alternating): fp64 numpy prologue + attention fwd + bwd, "
+                      f"{elapsed:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -111,6 +111,16 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
                       void* workspace, size_t workspace_bytes, nc_stream stream);
 
 /*
+ * Measurement aid. While set on the calling thread, every nc_attn_bwd call
+ * records begin_event on its stream just before its main kernel (the one
+ * that forms dK, dV and the dQ contributions) and end_event just after it,
+ * so a caller can time that kernel alone with hipEventElapsedTime. Both are
+ * hipEvent_t created by the caller; passing NULL for both clears the
+ * setting. Returns NC_ERR_INVALID_ARG if exactly one of them is NULL.
+ */
+nc_status nc_profile_bwd_main(void* begin_event, void* end_event);
+
+/*
  * Single-token decode against one layer's KV cache ("nanochat Admin &
  * Developer Guide", section 7 "KV cache": per-layer (B, T, H, D) cache with
  * int32 per-row lengths; section 6: single-token decode slices the key

@@ -160,6 +160,11 @@ def test_prologue_validation(L):
     assert g(BF16, 1, 16, 2, 1, 64, A, A, None, A, A, 32, 1e-6, A, A, A, None, None) == INVALID
 
 
+def test_profile_hook_validation(L):
+    assert L.nc_profile_bwd_main(A, None) == INVALID
+    assert L.nc_profile_bwd_main(None, None) == OK
+
+
 def test_error_message_is_per_thread(L):
     import threading
     assert fwd(L, q=None) == INVALID

@@ -21,6 +21,7 @@ bool decode_group_supported(int G);
 namespace {
 
 thread_local char g_msg[512] = "";
+thread_local hipEvent_t g_bwd_ev[2] = {nullptr, nullptr};
 
 nc_status fail(nc_status s, const char* fmt, ...) {
   va_list ap;
@@ -176,7 +177,18 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
                   dt == NC_BF16 ? (float*)((char*)workspace + delta_bytes) : nullptr,
                   B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f};
   hipStream_t s = (hipStream_t)stream;
-  return finish(dt == NC_BF16 ? nc::launch_attn_bwd_bf16(p, s) : nc::launch_attn_bwd_f32(p, s), s, "nc_attn_bwd");
+  return finish(dt == NC_BF16 ? nc::launch_attn_bwd_bf16(p, s, g_bwd_ev[0], g_bwd_ev[1])
+                                : nc::launch_attn_bwd_f32(p, s, g_bwd_ev[0], g_bwd_ev[1]),
+                s, "nc_attn_bwd");
+}
+
+nc_status nc_profile_bwd_main(void* begin_event, void* end_event) {
+  if ((begin_event == nullptr) != (end_event == nullptr))
+    return fail(NC_ERR_INVALID_ARG, "begin_event and end_event must both be set or both be NULL");
+  g_bwd_ev[0] = (hipEvent_t)begin_event;
+  g_bwd_ev[1] = (hipEvent_t)end_event;
+  g_msg[0] = 0;
+  return NC_OK;
 }
 
 size_t nc_attn_decode_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, int D, int T_max) {

@@ -414,48 +414,55 @@ hipError_t launch_pre(const BwdParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t record(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
+
 template <int D>
-hipError_t launch_bf16(const BwdParams& p, hipStream_t s) {
+hipError_t launch_bf16(const BwdParams& p, hipStream_t s, hipEvent_t eb, hipEvent_t ee) {
   hipError_t e = launch_pre<D, true>(p, s);
   if (e != hipSuccess) return e;
   const int nkt = (p.T + BWD_BN - 1) / BWD_BN;
+  if ((e = record(eb, s)) != hipSuccess) return e;
   attn_bwd_bf16_kernel<D><<<nkt * p.Hkv * p.B, BWD_THREADS, 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if ((e = record(ee, s)) != hipSuccess) return e;
   const long n8 = (long)p.B * p.T * p.H * D / 8;
   bwd_post_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, s>>>(p.dq_acc, (unsigned short*)p.dq, n8);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_f32(const BwdParams& p, hipStream_t s) {
+hipError_t launch_f32(const BwdParams& p, hipStream_t s, hipEvent_t eb, hipEvent_t ee) {
   hipError_t e = launch_pre<D, false>(p, s);
   if (e != hipSuccess) return e;
+  if ((e = record(eb, s)) != hipSuccess) return e;
   bwd_dkdv_f32_kernel<D><<<dim3((p.T + 63) / 64, p.Hkv, p.B), 64, 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   bwd_dq_f32_kernel<D><<<dim3((p.T + 63) / 64, p.H, p.B), 64, 0, s>>>(p);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return record(ee, s);
 }
 
 }  // namespace
 
-hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s) {
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s, hipEvent_t eb, hipEvent_t ee) {
   switch (p.D) {
-    case 32: return launch_bf16<32>(p, s);
-    case 64: return launch_bf16<64>(p, s);
-    case 128: return launch_bf16<128>(p, s);
+    case 32: return launch_bf16<32>(p, s, eb, ee);
+    case 64: return launch_bf16<64>(p, s, eb, ee);
+    case 128: return launch_bf16<128>(p, s, eb, ee);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s) {
+hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s, hipEvent_t eb, hipEvent_t ee) {
   BwdParams q = p;
   q.dq_acc = nullptr;
   switch (p.D) {
-    case 32: return launch_f32<32>(q, s);
-    case 64: return launch_f32<64>(q, s);
-    case 128: return launch_f32<128>(q, s);
+    case 32: return launch_f32<32>(q, s, eb, ee);
+    case 64: return launch_f32<64>(q, s, eb, ee);
+    case 128: return launch_f32<128>(q, s, eb, ee);
     default: return hipErrorInvalidValue;
   }
 }

@@ -71,8 +71,9 @@ constexpr int kDecodeSplit = 256;
 
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const FwdParams& p, hipStream_t s);
-hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s);
-hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s);
+// ev_begin / ev_end (may be null) are recorded around the main kernel(s).
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end);
+hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t s);
 hipError_t launch_rope_table(int T_rope, int D, double base, float* c, float* sn, hipStream_t s);
 hipError_t launch_prologue(const PrologueParams& p, bool bf16, bool backward, hipStream_t s);

@@ -22,7 +22,7 @@ STATUS = {0: "NC_OK", 1: "NC_ERR_INVALID_ARG", 2: "NC_ERR_UNSUPPORTED", 3: "NC_E
 # every symbol include/ncattn.h declares
 EXPORTS = (
     "nc_abi_version", "nc_status_string", "nc_last_error_message",
-    "nc_attn_fwd", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd",
+    "nc_attn_fwd", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd", "nc_profile_bwd_main",
     "nc_attn_decode_workspace_bytes", "nc_attn_decode",
     "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd",
 )
@@ -46,6 +46,7 @@ _SIGS = {
     "nc_attn_fwd": ([_i] * 6 + [_p, _p, _p, _i, _f, _p, _p, _p], _i),
     "nc_attn_bwd_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_bwd": ([_i] * 6 + [_p] * 6 + [_i, _f] + [_p] * 3 + [_p, _sz, _p], _i),
+    "nc_profile_bwd_main": ([_p, _p], _i),
     "nc_attn_decode_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_decode": ([_i] * 6 + [_p] * 4 + [_i, _f, _p, _p, _p, _sz, _p], _i),
     "nc_rope_table": ([_i, _i, _d, _p, _p, _p], _i),
@@ -146,6 +147,15 @@ def nc_attn_bwd(q, k, v, out, lse, dout, window, scale, dq=None, dk=None, dv=Non
                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _raise_on("nc_attn_bwd", st)
     return dq, dk, dv
+
+
+def nc_profile_bwd_main(begin_event=None, end_event=None):
+    """Record two torch.cuda.Event objects (already recorded once, so that
+    they exist) around the main kernel of later nc_attn_bwd calls on this
+    thread; call with no arguments to stop."""
+    b = begin_event.cuda_event if begin_event is not None else None
+    e = end_event.cuda_event if end_event is not None else None
+    _raise_on("nc_profile_bwd_main", lib().nc_profile_bwd_main(b, e))
 
 
 def nc_attn_decode_workspace_bytes(dtype_code, B, H, Hkv, D, T_max):
