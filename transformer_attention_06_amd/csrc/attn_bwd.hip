@@ -99,18 +99,17 @@ __global__ __launch_bounds__(256) void bwd_post_kernel(const float* __restrict__
 // --------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams p) {
-  constexpr int LD = D + 8;         // row stride (elements) of q/dO/K tiles in LDS
-  constexpr int DSLD = BWD_BM + 8;  // row stride of the dS^T tile [key][query]
+  constexpr int NC = D / 8;        // chunks per row of the q/dO/K tiles (swizzled)
+  constexpr int NCS = BWD_BM / 8;  // chunks per row of the dS^T tile [key][query]
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int CPR = D / 8;
-  constexpr int QLOADS = BWD_BM * CPR / BWD_THREADS;
-  constexpr int KLOADS = BWD_BN * CPR / BWD_THREADS;
+  constexpr int QLOADS = BWD_BM * NC / BWD_THREADS;
+  constexpr int KLOADS = BWD_BN * NC / BWD_THREADS;
   static_assert(QLOADS >= 1 && KLOADS >= 1, "tile/thread mismatch");
-  __shared__ __attribute__((aligned(16))) unsigned short k_lds[BWD_BN * LD];
-  __shared__ __attribute__((aligned(16))) unsigned short q_lds[BWD_BM * LD];
-  __shared__ __attribute__((aligned(16))) unsigned short do_lds[BWD_BM * LD];
-  __shared__ __attribute__((aligned(16))) unsigned short ds_lds[BWD_BN * DSLD];
+  __shared__ __attribute__((aligned(16))) unsigned short k_lds[BWD_BN * D];
+  __shared__ __attribute__((aligned(16))) unsigned short q_lds[BWD_BM * D];
+  __shared__ __attribute__((aligned(16))) unsigned short do_lds[BWD_BM * D];
+  __shared__ __attribute__((aligned(16))) unsigned short ds_lds[BWD_BN * BWD_BM];
   __shared__ float lse2_lds[BWD_BM];
   __shared__ float delta_lds[BWD_BM];
 
@@ -140,11 +139,11 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
 #pragma unroll
   for (int n = 0; n < KLOADS; ++n) {
     const int c = tid + n * BWD_THREADS;
-    const int row = c / CPR, ch = c - row * CPR;
+    const int row = c / NC, ch = c - row * NC;
     const int j = j0 + row;
     u32x4 w = {0u, 0u, 0u, 0u};
     if (j < T) w = *(const u32x4*)(kp + (size_t)j * kvrs + ch * 8);
-    *(u32x4*)(k_lds + row * LD + ch * 8) = w;
+    *(u32x4*)(k_lds + swz_off<NC>(row, ch * 8)) = w;
   }
   // K and V fragments of this lane's key: lane (li, hh) holds x[kj][16 s + 8 hh + e].
   bf16x8 kf[NS], vf[NS];
@@ -169,131 +168,140 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
   const bool full = p.window <= 0;
   const int win = p.window;
   const int i_last = full ? T - 1 : min(T - 1, j0 + BWD_BN - 1 + win - 1);
-  const int it_begin = j0 / BWD_BM, it_end = i_last / BWD_BM;
-  // transpose-read lane offsets: rows r0 + t16/4, columns c0 + 16 (grp&1) + 4 (t16&3)
+  const int it_begin = j0 / BWD_BM, n_it = i_last / BWD_BM - it_begin + 1;
+  const int n_steps = G * n_it;
   const int tr_row = t16 >> 2;
   const int tr_col = 16 * (grp & 1) + 4 * (t16 & 3);
 
-  for (int hq = 0; hq < G; ++hq) {
+  // Registers holding the next step's q/dO tile rows, lse and delta.
+  u32x4 qreg[QLOADS], oreg[QLOADS];
+  float lreg = INFINITY, dreg = 0.f;
+  auto prefetch = [&](int step) {
+    const int hq = step / n_it;
+    const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
     const int h = g * G + hq;
     const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
     const unsigned short* dop = (const unsigned short*)p.dout + (size_t)b * T * qrs + (size_t)h * D;
-    const float* lsep = p.lse + ((size_t)b * p.H + h) * T;
-    const float* delp = p.delta + ((size_t)b * p.H + h) * T;
-    float* dqa = p.dq_acc + (size_t)b * T * qrs + (size_t)h * D;
-
-    for (int it = it_begin; it <= it_end; ++it) {
-      const int i0 = it * BWD_BM;
-      __syncthreads();
 #pragma unroll
-      for (int n = 0; n < QLOADS; ++n) {
-        const int c = tid + n * BWD_THREADS;
-        const int row = c / CPR, ch = c - row * CPR;
-        const int i = i0 + row;
-        u32x4 a = {0u, 0u, 0u, 0u}, o = {0u, 0u, 0u, 0u};
-        if (i < T) {
-          a = *(const u32x4*)(qp + (size_t)i * qrs + ch * 8);
-          o = *(const u32x4*)(dop + (size_t)i * qrs + ch * 8);
-        }
-        *(u32x4*)(q_lds + row * LD + ch * 8) = a;
-        *(u32x4*)(do_lds + row * LD + ch * 8) = o;
+    for (int n = 0; n < QLOADS; ++n) {
+      const int c = tid + n * BWD_THREADS;
+      const int row = c / NC, ch = c - row * NC;
+      const int i = i0 + row;
+      qreg[n] = (u32x4){0u, 0u, 0u, 0u};
+      oreg[n] = (u32x4){0u, 0u, 0u, 0u};
+      if (i < T) {
+        qreg[n] = *(const u32x4*)(qp + (size_t)i * qrs + ch * 8);
+        oreg[n] = *(const u32x4*)(dop + (size_t)i * qrs + ch * 8);
       }
-      if (tid < BWD_BM) {
-        const int i = i0 + tid;
-        lse2_lds[tid] = i < T ? lsep[i] * kLog2e : INFINITY;
-        delta_lds[tid] = i < T ? delp[i] : 0.f;
-      }
-      __syncthreads();
+    }
+    if (tid < BWD_BM) {
+      const int i = i0 + tid;
+      const size_t li2 = ((size_t)b * p.H + h) * T + i;
+      lreg = i < T ? p.lse[li2] * kLog2e : INFINITY;
+      dreg = i < T ? p.delta[li2] : 0.f;
+    }
+  };
 
-      const bool any = (kw <= i0 + BWD_BM - 1) && (full || kw + 31 > i0 - win);
-      const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win);
-      f32x16 sacc[2], dpacc[2];
+  prefetch(0);
+  for (int step = 0; step < n_steps; ++step) {
+    const int hq = step / n_it;
+    const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
+    const int h = g * G + hq;
+    __syncthreads();  // every reader of the previous step's tiles is done
+#pragma unroll
+    for (int n = 0; n < QLOADS; ++n) {
+      const int c = tid + n * BWD_THREADS;
+      const int row = c / NC, ch = c - row * NC;
+      *(u32x4*)(q_lds + swz_off<NC>(row, ch * 8)) = qreg[n];
+      *(u32x4*)(do_lds + swz_off<NC>(row, ch * 8)) = oreg[n];
+    }
+    if (tid < BWD_BM) {
+      lse2_lds[tid] = lreg;
+      delta_lds[tid] = dreg;
+    }
+    __syncthreads();
+    if (step + 1 < n_steps) prefetch(step + 1);
+
+    const bool any = (kw <= i0 + BWD_BM - 1) && (full || kw + 31 > i0 - win);
+    const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win);
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib) {
+      float dsr[16];
       if (any) {
+        f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) {
-          sacc[ib] = (f32x16){};
-          dpacc[ib] = (f32x16){};
-#pragma unroll
-          for (int st = 0; st < NS; ++st) {
-            const bf16x8 aq = *(const bf16x8*)(q_lds + (32 * ib + li) * LD + 16 * st + 8 * hh);
-            sacc[ib] = mfma32(aq, kf[st], sacc[ib]);
-            const bf16x8 ad = *(const bf16x8*)(do_lds + (32 * ib + li) * LD + 16 * st + 8 * hh);
-            dpacc[ib] = mfma32(ad, vf[st], dpacc[ib]);
-          }
+        for (int st = 0; st < NS; ++st) {
+          const bf16x8 aq = *(const bf16x8*)(q_lds + swz_off<NC>(32 * ib + li, 16 * st + 8 * hh));
+          sacc = mfma32(aq, kf[st], sacc);
+          const bf16x8 ad = *(const bf16x8*)(do_lds + swz_off<NC>(32 * ib + li, 16 * st + 8 * hh));
+          dpacc = mfma32(ad, vf[st], dpacc);
         }
-        // sacc[ib][r] = S[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][key kj]
-        float pr[2][16], dsr[2][16];
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int il = 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3);
-            float pv = exp2_fast(fmaf(sacc[ib][r], p.scale_log2, -lse2_lds[il]));
-            if (!interior) {
-              const int i = i0 + il;
-              const bool vis = (kj <= i) && (full || kj > i - win);
-              if (!vis) pv = 0.f;
-            }
-            pr[ib][r] = pv;
-            dsr[ib][r] = pv * (dpacc[ib][r] - delta_lds[il]);
-          }
-        // dV^T += dO^T P and dK^T += Q^T dS over this tile's 64 queries.
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const bf16x8 pb = to_bf16x8(&pr[ib][8 * u]);
-            const bf16x8 sb = to_bf16x8(&dsr[ib][8 * u]);
-            const int roff = (32 * ib + 16 * u + 4 * hh + tr_row) * LD + tr_col;
-#pragma unroll
-            for (int d = 0; d < ND; ++d) {
-              const s16x4 o1 = lds_read_tr16(do_lds + roff + 32 * d);
-              const s16x4 o2 = lds_read_tr16(do_lds + roff + 32 * d + 8 * LD);
-              dv[d] = mfma32(cat_bf16x8(o1, o2), pb, dv[d]);
-              const s16x4 q1 = lds_read_tr16(q_lds + roff + 32 * d);
-              const s16x4 q2 = lds_read_tr16(q_lds + roff + 32 * d + 8 * LD);
-              dk[d] = mfma32(cat_bf16x8(q1, q2), sb, dk[d]);
-            }
-          }
-        // dS^T -> LDS: row = key (wave*32 + li), columns = the 4 queries of each group.
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            u32x2 w;
-            w[0] = pack2_bf16(dsr[ib][4 * rg], dsr[ib][4 * rg + 1]);
-            w[1] = pack2_bf16(dsr[ib][4 * rg + 2], dsr[ib][4 * rg + 3]);
-            *(u32x2*)(ds_lds + (wave * 32 + li) * DSLD + 32 * ib + 8 * rg + 4 * hh) = w;
-          }
-      } else {
-#pragma unroll
-        for (int ib = 0; ib < 2; ++ib)
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg)
-            *(u32x2*)(ds_lds + (wave * 32 + li) * DSLD + 32 * ib + 8 * rg + 4 * hh) = (u32x2){0u, 0u};
-      }
-      __syncthreads();
-
-      // dQ[i][d] = sum over the 128 keys of dS[i][j] K[j][d]; output blocks
-      // (ib, db) are dealt to the waves.
-      for (int n = wave; n < 2 * ND; n += 4) {
-        const int ib = n / ND, db = n - (n / ND) * ND;
-        f32x16 acc = (f32x16){};
-#pragma unroll
-        for (int u = 0; u < BWD_BN / 16; ++u) {
-          const int r0 = 16 * u + 8 * hh + tr_row;
-          const s16x4 a1 = lds_read_tr16(ds_lds + r0 * DSLD + 32 * ib + tr_col);
-          const s16x4 a2 = lds_read_tr16(ds_lds + (r0 + 4) * DSLD + 32 * ib + tr_col);
-          const s16x4 b1 = lds_read_tr16(k_lds + r0 * LD + 32 * db + tr_col);
-          const s16x4 b2 = lds_read_tr16(k_lds + (r0 + 4) * LD + 32 * db + tr_col);
-          acc = mfma32(cat_bf16x8(a1, a2), cat_bf16x8(b1, b2), acc);
-        }
-        // acc[r] = dQ[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][d = 32 db + li]
+        // sacc[r] = S[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][key kj]
+        float pr[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int i = i0 + 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3);
-          if (i < T) atomicAdd(dqa + (size_t)i * qrs + 32 * db + li, acc[r] * p.scale);
+          const int il = 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3);
+          float pv = exp2_fast(fmaf(sacc[r], p.scale_log2, -lse2_lds[il]));
+          if (!interior) {
+            const int i = i0 + il;
+            const bool vis = (kj <= i) && (full || kj > i - win);
+            if (!vis) pv = 0.f;
+          }
+          pr[r] = pv;
+          dsr[r] = pv * (dpacc[r] - delta_lds[il]);
         }
+        // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const bf16x8 pb = to_bf16x8(&pr[8 * u]);
+          const bf16x8 sb = to_bf16x8(&dsr[8 * u]);
+          const int r1 = 32 * ib + 16 * u + 4 * hh + tr_row;
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const int col = 32 * d + tr_col;
+            const s16x4 o1 = lds_read_tr16(do_lds + swz_off<NC>(r1, col));
+            const s16x4 o2 = lds_read_tr16(do_lds + swz_off<NC>(r1 + 8, col));
+            dv[d] = mfma32(cat_bf16x8(o1, o2), pb, dv[d]);
+            const s16x4 q1 = lds_read_tr16(q_lds + swz_off<NC>(r1, col));
+            const s16x4 q2 = lds_read_tr16(q_lds + swz_off<NC>(r1 + 8, col));
+            dk[d] = mfma32(cat_bf16x8(q1, q2), sb, dk[d]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dsr[r] = 0.f;
+      }
+      // dS^T -> LDS: row = key (wave*32 + li), 4 consecutive queries per store.
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        u32x2 w;
+        w[0] = pack2_bf16(dsr[4 * rg], dsr[4 * rg + 1]);
+        w[1] = pack2_bf16(dsr[4 * rg + 2], dsr[4 * rg + 3]);
+        *(u32x2*)(ds_lds + swz_off<NCS>(wave * 32 + li, 32 * ib + 8 * rg + 4 * hh)) = w;
+      }
+    }
+    __syncthreads();
+
+    // dQ[i][d] = sum over the 128 keys of dS[i][j] K[j][d]; output blocks
+    // (ib, db) are dealt to the waves.
+    float* dqa = p.dq_acc + (size_t)b * T * qrs + (size_t)h * D;
+    for (int n = wave; n < 2 * ND; n += 4) {
+      const int ib = n / ND, db = n - (n / ND) * ND;
+      f32x16 acc = (f32x16){};
+#pragma unroll
+      for (int u = 0; u < BWD_BN / 16; ++u) {
+        const int r0 = 16 * u + 8 * hh + tr_row;
+        const s16x4 a1 = lds_read_tr16(ds_lds + swz_off<NCS>(r0, 32 * ib + tr_col));
+        const s16x4 a2 = lds_read_tr16(ds_lds + swz_off<NCS>(r0 + 4, 32 * ib + tr_col));
+        const s16x4 b1 = lds_read_tr16(k_lds + swz_off<NC>(r0, 32 * db + tr_col));
+        const s16x4 b2 = lds_read_tr16(k_lds + swz_off<NC>(r0 + 4, 32 * db + tr_col));
+        acc = mfma32(cat_bf16x8(a1, a2), cat_bf16x8(b1, b2), acc);
+      }
+      // acc[r] = dQ[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][d = 32 db + li]
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = i0 + 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (i < T) atomicAdd(dqa + (size_t)i * qrs + 32 * db + li, acc[r] * p.scale);
       }
     }
   }

@@ -8,8 +8,10 @@
 //
 // bf16 kernel (flash-style, one pass over the keys with an online softmax):
 //   * workgroup = 128 queries of one (b, h); 4 waves, 32 queries each;
-//   * K/V tiles of 64 keys staged in LDS, the next tile prefetched into
-//     registers while the current one is consumed;
+//   * K/V tiles of 64 keys copied by buffer-to-LDS loads straight into a
+//     double-buffered, XOR-swizzled LDS tile, the next tile in flight while
+//     the current one is consumed; all LDS addresses are per-lane constants
+//     plus immediates (the loop is unrolled over the two buffers);
 //   * S^T = K Q^T on 32x32x16 bf16 MFMA, so that each lane owns one query
 //     column: the row max and row sum need no cross-lane reduction except
 //     one exchange between the two half-waves;
@@ -17,11 +19,15 @@
 //     B-operand layout of O^T += V^T P^T (the contraction index is permuted
 //     identically on both operands), and V^T is read with LDS transpose
 //     reads;
+//   * the running max only moves when a tile exceeds it by more than a
+//     factor 2^8, so the O rescale is rare;
 //   * tiles entirely outside the causal band or window are never visited;
 //     element masks are applied only on tiles that cut the band's edges.
 // f32 kernel: plain per-query loop in float32, for the fp32 configurations.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -35,14 +41,15 @@ constexpr int FWD_THREADS = 256;
 
 template <int D>
 __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams p) {
-  constexpr int LD = D + 8;  // LDS row stride (elements): 16-byte pad per row
+  constexpr int NC = D / 8;  // 16-byte chunks per row (LDS tiles are swizzled, unpadded)
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  constexpr int LOADS = FWD_BN * CPR / FWD_THREADS;
-  static_assert(LOADS >= 1 && FWD_BN * CPR % FWD_THREADS == 0, "tile/thread mismatch");
-  __shared__ __attribute__((aligned(16))) unsigned short k_lds[FWD_BN * LD];
-  __shared__ __attribute__((aligned(16))) unsigned short v_lds[FWD_BN * LD];
+  constexpr int TILE = FWD_BN * D;        // elements of one K or V tile
+  constexpr int RPI = 64 / NC;            // tile rows per direct-to-LDS instruction (64 lanes x 16 B)
+  constexpr int IPW = FWD_BN / RPI / 4;   // such instructions per wave per tensor per tile
+  static_assert(IPW >= 1 && FWD_BN % (4 * RPI) == 0, "tile/wave mismatch");
+  // [buffer][K or V][tile]: the next tile streams into one buffer while the other is read
+  __shared__ __attribute__((aligned(16))) unsigned short kv_lds[2][2][TILE];
 
   const int T = p.T;
   const int nqt = (T + FWD_BM - 1) / FWD_BM;
@@ -54,18 +61,22 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   const int g = h / (p.H / p.Hkv);
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hh = lane >> 5;
+  const int grp = lane >> 4, t16 = lane & 15;
   const int q0 = qt * FWD_BM;
   const int qw = q0 + wave * 32;
   const int qi = qw + li;
   const bool q_valid = qi < T;
 
   const size_t qrs = (size_t)p.H * D;
-  const size_t kvrs = (size_t)p.Hkv * D;
+  const unsigned kvrs = (unsigned)(p.Hkv * D);  // elements between consecutive positions
   const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
   const unsigned short* kp = (const unsigned short*)p.k + (size_t)b * T * kvrs + (size_t)g * D;
   const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * T * kvrs + (size_t)g * D;
+  // this (b, g)'s rows 0 .. T-1 span (T - 1) * kvrs + D elements
+  const unsigned span = (unsigned)(((size_t)(T - 1) * kvrs + D) * 2);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, span), vrs = make_rsrc(vp, span);
 
   // Q as the B operand of S^T = K Q^T: lane (li, hh) holds q[qi][16 s + 8 hh + e].
   bf16x8 qf[NS];
@@ -78,118 +89,156 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
 
   const bool full = p.window <= 0;
   const int win = p.window;
+  // key j is visible to query i iff (unsigned)(i - j) < wlim
+  const unsigned wlim = full ? 0x80000000u : (unsigned)win;
   const int kv_hi = min(T - 1, q0 + FWD_BM - 1);
   const int kv_lo = full ? 0 : max(0, q0 - win + 1);
   const int t_begin = kv_lo / FWD_BN, t_end = kv_hi / FWD_BN;
 
-  float m2 = -INFINITY;  // running max of scale*log2(e)*s for this query
+  // Tile loads: lane l of instruction n writes tile row (inst*RPI + l/NC),
+  // physical chunk l%NC, which holds logical chunk (l%NC) ^ swz(row). The
+  // lane's source offset inside the tile is fixed; the tile and instruction
+  // offsets are uniform. The last tile may run past T: its rows are clamped
+  // to T-1 (finite data, masked for every valid query).
+  unsigned ld_off[IPW];
+  int ld_row[IPW], ld_ch[IPW];
+#pragma unroll
+  for (int n = 0; n < IPW; ++n) {
+    const int row = (wave * IPW + n) * RPI + lane / NC;
+    ld_row[n] = row;
+    ld_ch[n] = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
+    ld_off[n] = (unsigned)(row * kvrs + ld_ch[n] * 8) * 2u;
+  }
+  auto issue_tile = [&](int jt, int buf) {
+    const int j0 = jt * FWD_BN;
+    if (j0 + FWD_BN <= T) {
+      const unsigned so = (unsigned)j0 * kvrs * 2u;
+#pragma unroll
+      for (int n = 0; n < IPW; ++n) {
+        void* dk = &kv_lds[buf][0][(wave * IPW + n) * RPI * D];
+        void* dv = &kv_lds[buf][1][(wave * IPW + n) * RPI * D];
+        buf2lds16(krs, ld_off[n], so, dk);
+        buf2lds16(vrs, ld_off[n], so, dv);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < IPW; ++n) {
+        const int j = min(j0 + ld_row[n], T - 1);
+        const unsigned vo = (unsigned)(j * kvrs + ld_ch[n] * 8) * 2u;
+        buf2lds16(krs, vo, 0u, &kv_lds[buf][0][(wave * IPW + n) * RPI * D]);
+        buf2lds16(vrs, vo, 0u, &kv_lds[buf][1][(wave * IPW + n) * RPI * D]);
+      }
+    }
+  };
+
+  // Per-lane LDS element offsets (tile-relative), fixed for the whole kernel:
+  // K operand rows li (+32 for the second key block) at chunk 2 st + hh;
+  // V^T transpose reads at rows 4 hh + t16/4 (+8) (+16 u + 32 jb), columns
+  // 32 d + 16 (grp & 1) + 4 (t16 & 3).
+  int koff[NS], voff1[ND], voff2[ND];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) koff[st] = swz_off<NC>(li, 16 * st + 8 * hh);
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    const int col = 32 * d + 16 * (grp & 1) + 4 * (t16 & 3);
+    voff1[d] = swz_off<NC>(4 * hh + (t16 >> 2), col);
+    voff2[d] = swz_off<NC>(4 * hh + (t16 >> 2) + 8, col);
+  }
+
+  float m2 = -INFINITY;  // running reference max (log2 units) for this query
   float lsum = 0.f;      // running sum over this lane's half of the keys
   f32x16 o[ND];
 #pragma unroll
   for (int d = 0; d < ND; ++d) o[d] = (f32x16){};
 
-  u32x4 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int jt) {
-#pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      const int c = tid + n * FWD_THREADS;
-      const int row = c / CPR, ch = c - row * CPR;
-      const int j = jt * FWD_BN + row;
-      if (j < T) {
-        kreg[n] = *(const u32x4*)(kp + (size_t)j * kvrs + ch * 8);
-        vreg[n] = *(const u32x4*)(vp + (size_t)j * kvrs + ch * 8);
-      } else {
-        kreg[n] = (u32x4){0u, 0u, 0u, 0u};
-        vreg[n] = (u32x4){0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int n = 0; n < LOADS; ++n) {
-      const int c = tid + n * FWD_THREADS;
-      const int row = c / CPR, ch = c - row * CPR;
-      *(u32x4*)(k_lds + row * LD + ch * 8) = kreg[n];
-      *(u32x4*)(v_lds + row * LD + ch * 8) = vreg[n];
-    }
-  };
-
-  const int grp = lane >> 4, t16 = lane & 15;
-  // per-lane offset of the transpose read of V^T (rows 4 hh + t16/4, columns 16 (grp&1) + 4 (t16&3))
-  const int vtr_off = (4 * hh + (t16 >> 2)) * LD + 16 * (grp & 1) + 4 * (t16 & 3);
-
-  load_tile(t_begin);
-  for (int jt = t_begin; jt <= t_end; ++jt) {
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (jt < t_end) load_tile(jt + 1);
+  auto tile = [&](int jt, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
+    wait_vmem();
+    __syncthreads();  // tile jt is in buf; every wave is done with the other buffer
+    if (jt < t_end) issue_tile(jt + 1, buf ^ 1);
+    const unsigned short* kl = kv_lds[buf][0];
+    const unsigned short* vl = kv_lds[buf][1];
 
     const int j0 = jt * FWD_BN;
     const bool any = (j0 <= qw + 31) && (full || j0 + FWD_BN - 1 > qw - win);
-    if (!any) continue;
+    if (!any) return;
     const bool interior = (j0 + FWD_BN - 1 <= qw) && (full || j0 > qw + 31 - win);
 
-    f32x16 s[2];
+    f32x16 s[2] = {(f32x16){}, (f32x16){}};
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      s[jb] = (f32x16){};
+    for (int st = 0; st < NS; ++st)
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        const bf16x8 a = *(const bf16x8*)(k_lds + (jb * 32 + li) * LD + 16 * st + 8 * hh);
+      for (int jb = 0; jb < 2; ++jb) {
+        const bf16x8 a = *(const bf16x8*)(kl + koff[st] + jb * 32 * D);
         s[jb] = mfma32(a, qf[st], s[jb]);
       }
-    }
     // s[jb][r] = S[key j0 + 32 jb + 8 (r/4) + 4 hh + r%4][query qi]
     if (!interior) {
+      const int base = qi - j0 - 4 * hh;
 #pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = j0 + 32 * jb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          const bool vis = (j <= qi) && (full || j > qi - win);
-          if (!vis) s[jb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if ((unsigned)(base - (32 * jb + 8 * (r >> 2) + (r & 3))) >= wlim) s[jb][r] = -INFINITY;
     }
-    float mx = s[0][0];
+    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[1][0]);
 #pragma unroll
-    for (int jb = 0; jb < 2; ++jb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jb][r]);
+    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
     mx = fmaxf(mx, shfl_xor(mx, 32));
-    const float m_new = fmaxf(m2, mx * p.scale_log2);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(m2 - m_use);
-    m2 = m_new;
+    // The reference max only moves up when the tile max exceeds it by more than
+    // 8 (a factor 2^8): the exponentials stay <= 256 and O is rescaled rarely.
+    const float mt = mx * p.scale_log2;
+    const bool raise = mt > m2 + 8.f;
+    float alpha = 1.f;
+    if (raise) {
+      alpha = exp2_fast(m2 - mt);
+      m2 = mt;
+    }
+    if (__any(raise)) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+      lsum *= alpha;
+    }
+    const float m_use = (m2 == -INFINITY) ? 0.f : m2;
 
-    float pv[2][16];
-    float rs = 0.f;
+    // P^T as bf16 B operands (8 per 16 keys); row sums of the float values.
+    unsigned pw[2][8];
+    float rs0 = 0.f, rs1 = 0.f;
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[jb][r] = exp2_fast(fmaf(s[jb][r], p.scale_log2, -m_use));
-        rs += pv[jb][r];
+      for (int r = 0; r < 16; r += 2) {
+        const float e0 = exp2_fast(fmaf(s[jb][r], p.scale_log2, -m_use));
+        const float e1 = exp2_fast(fmaf(s[jb][r + 1], p.scale_log2, -m_use));
+        pw[jb][r >> 1] = pk_bf16(e0, e1);
+        rs0 += e0;
+        rs1 += e1;
       }
-    lsum = fmaf(lsum, alpha, rs);
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[d][r] *= alpha;
+    lsum += rs0 + rs1;
 
+    // O^T += V^T P^T over the tile's 64 keys.
 #pragma unroll
     for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        const bf16x8 pb = to_bf16x8(&pv[jb][8 * u]);
-        const unsigned short* vb = v_lds + (32 * jb + 16 * u) * LD + vtr_off;
+        const u32x4 pq = {pw[jb][4 * u], pw[jb][4 * u + 1], pw[jb][4 * u + 2], pw[jb][4 * u + 3]};
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, pq);
+        const int rb = (32 * jb + 16 * u) * D;
 #pragma unroll
         for (int d = 0; d < ND; ++d) {
-          const s16x4 x1 = lds_read_tr16(vb + 32 * d);
-          const s16x4 x2 = lds_read_tr16(vb + 32 * d + 8 * LD);
+          const s16x4 x1 = lds_read_tr16(vl + voff1[d] + rb);
+          const s16x4 x2 = lds_read_tr16(vl + voff2[d] + rb);
           o[d] = mfma32(cat_bf16x8(x1, x2), pb, o[d]);
         }
       }
+  };
+
+  issue_tile(t_begin, 0);
+  for (int jt = t_begin; jt <= t_end; jt += 2) {
+    tile(jt, std::integral_constant<int, 0>{});
+    if (jt + 1 <= t_end) tile(jt + 1, std::integral_constant<int, 1>{});
   }
 
   const float lt = lsum + shfl_xor(lsum, 32);
@@ -201,8 +250,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         u32x2 w;
-        w[0] = pack2_bf16(o[d][4 * rg] * inv, o[d][4 * rg + 1] * inv);
-        w[1] = pack2_bf16(o[d][4 * rg + 2] * inv, o[d][4 * rg + 3] * inv);
+        w[0] = pk_bf16(o[d][4 * rg] * inv, o[d][4 * rg + 1] * inv);
+        w[1] = pk_bf16(o[d][4 * rg + 2] * inv, o[d][4 * rg + 3] * inv);
         *(u32x2*)(op + 32 * d + 8 * rg + 4 * hh) = w;
       }
     if (hh == 0) p.lse[((size_t)b * p.H + h) * T + qi] = (m2 + __builtin_log2f(lt)) * kLn2;

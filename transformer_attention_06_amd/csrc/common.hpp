@@ -47,10 +47,50 @@ __device__ __forceinline__ u32x4 pack8_bf16(const float* f) {
   return w;
 }
 
-// MFMA operand from 8 floats (element e of the operand = f[e]).
+// MFMA operand from 8 floats (element e of the operand = f[e]); packed
+// two-at-a-time round-to-nearest-even conversions.
 __device__ __forceinline__ bf16x8 to_bf16x8(const float* f) {
-  return __builtin_bit_cast(bf16x8, pack8_bf16(f));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 a = __builtin_convertvector((f32x2){f[0], f[1]}, bf16x2);
+  bf16x2 b = __builtin_convertvector((f32x2){f[2], f[3]}, bf16x2);
+  bf16x2 c = __builtin_convertvector((f32x2){f[4], f[5]}, bf16x2);
+  bf16x2 d = __builtin_convertvector((f32x2){f[6], f[7]}, bf16x2);
+  return (bf16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
+// Two floats -> one dword of two bf16 (lo first), one packed conversion.
+__device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes land at lds_base + 16 * l, lds_base being wave-uniform.
+__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
+                                   (void __attribute__((address_space(3)))*)((size_t)lds_base), 16, 0, 0);
+}
+// Raw buffer resource over [base, base + bytes) (no swizzle, no stride).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// Direct buffer -> LDS copy of 16 bytes per lane: lane l's bytes at
+// base + voffset + soffset land at lds_base + 16 * l (lds_base wave-uniform).
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, unsigned voffset, unsigned soffset,
+                                          void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)((size_t)lds_base), 16,
+                                           voffset, soffset, 0, 0);
+}
+// sum of the two bf16 halves of w, plus c (v_dot2_f32_bf16 against (1, 1))
+__device__ __forceinline__ float add2_bf16(unsigned w, float c) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, c, false);
+}
+
+// Wait until all of this wave's global loads (including direct-to-LDS ones) completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
 
 // ---------------------------------------------------------------------------
 // Exponentials: v_exp_f32 computes 2^x; callers fold log2(e) into their scale.
@@ -85,6 +125,24 @@ __device__ __forceinline__ bf16x8 cat_bf16x8(s16x4 a, s16x4 b) {
 // C[8*(r/4) + 4h + r%4][l%32].
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS tile layout: rows of NC 16-byte chunks (NC = elements per row / 8), no
+// padding; chunk c of row r is stored at chunk position c ^ swz<NC>(r). The
+// permutation makes both access patterns the kernels use conflict-free on
+// the 64-bank LDS: 16 consecutive rows read at one logical chunk (MFMA
+// operand rows, ds_read_b128) land on 16 distinct bank groups, and the
+// 4 rows x 4 chunks read by 32 lanes of a transpose read do as well.
+template <int NC>
+__device__ __forceinline__ int swz(int r) {
+  if (NC >= 16) return 4 * (r & 3) + ((r >> 2) & 3);
+  if (NC == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  return (r >> 2) & 3;
+}
+// Element offset of logical (row, col) in a swizzled tile with NC chunks per row.
+template <int NC>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return r * (NC * 8) + ((((col >> 3) ^ swz<NC>(r)) & (NC - 1)) << 3) + (col & 7);
 }
 
 // Blocks -> XCD-contiguous logical ids. Workgroups are dealt to the 8 XCDs
