@@ -97,8 +97,9 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
  *   dv_j = sum_{h in group} sum_i P_ij dout_i.
  * dk/dv are summed over the query heads of each group. dq/dk/dv are fully
  * overwritten. q, k, v, out, lse must be those of nc_attn_fwd with the same
- * window and scale. The float32 workspace holds delta [B,H,T] and a dq
- * accumulator [B,T,H,D]; its size is nc_attn_bwd_workspace_bytes().
+ * window and scale. The float32 workspace holds delta [B,H,T], lse*log2(e)
+ * [B,H,T] and (bf16) a dq accumulator [B,T,H,D]; its size is
+ * nc_attn_bwd_workspace_bytes().
  * dq accumulation uses float32 atomics, so dq can differ in the last bits
  * between runs; dk and dv are deterministic.
  */

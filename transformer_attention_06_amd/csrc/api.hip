@@ -147,10 +147,10 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
 
 size_t nc_attn_bwd_workspace_bytes(nc_dtype dt, int B, int T, int H, int Hkv, int D) {
   if (check_shape(dt, B, T, H, Hkv, D) != NC_OK) return 0;
-  size_t delta = (size_t)B * H * T * 4;
-  delta = (delta + 255) & ~(size_t)255;
+  size_t row_stats = (size_t)B * H * T * 4;  // delta, then lse * log2(e)
+  row_stats = (row_stats + 255) & ~(size_t)255;
   const size_t acc = dt == NC_BF16 ? (size_t)B * T * H * D * 4 : 0;
-  return delta + acc;
+  return 2 * row_stats + acc;
 }
 
 nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
@@ -172,9 +172,10 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
   if (!workspace || !aligned16(workspace) || workspace_bytes < need)
     return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   NC_TRY(check_device(nullptr));
-  size_t delta_bytes = ((size_t)B * H * T * 4 + 255) & ~(size_t)255;
+  const size_t stat_bytes = ((size_t)B * H * T * 4 + 255) & ~(size_t)255;
   nc::BwdParams p{q, k, v, out, lse, dout, dq, dk, dv, (float*)workspace,
-                  dt == NC_BF16 ? (float*)((char*)workspace + delta_bytes) : nullptr,
+                  (float*)((char*)workspace + stat_bytes),
+                  dt == NC_BF16 ? (float*)((char*)workspace + 2 * stat_bytes) : nullptr,
                   B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f};
   hipStream_t s = (hipStream_t)stream;
   return finish(dt == NC_BF16 ? nc::launch_attn_bwd_bf16(p, s, g_bwd_ev[0], g_bwd_ev[1])

@@ -13,7 +13,8 @@
 // plain chain rule through the softmax.)
 //
 // bf16 path, three kernels:
-//   pre:  delta_i = <dout_i, out_i> in float32; clear the float32 dq accumulator.
+//   pre:  delta_i = <dout_i, out_i> and lse_i * log2(e) in float32; clear the
+//         float32 dq accumulator.
 //   main: one workgroup per (b, kv head, 128-key tile); each of the 4 waves
 //         keeps 32 keys' K and V fragments in registers and accumulates dK^T
 //         and dV^T for them over every query head of the GQA group and every
@@ -21,12 +22,17 @@
 //         come out with one key column per lane, which is directly the
 //         B-operand layout of dV^T += dO^T P and dK^T += Q^T dS; dO^T and
 //         Q^T are LDS transpose reads. dS goes through LDS once so that
-//         dQ = dS K for the 128 keys is formed per workgroup and added to
-//         the float32 accumulator with one atomic per element.
+//         dQ = dS K for the 128 keys is formed per workgroup (each wave owns
+//         one 32-wide slice of d, whose K^T operand stays in registers) and
+//         added to the float32 accumulator with buffer atomics. Q/dO tiles
+//         and the per-row statistics stream into double-buffered LDS with
+//         buffer-to-LDS loads; LDS addresses are per-lane constants.
 //   post: dq = bf16(scale-applied accumulator).
 // f32 path: plain per-key (dk, dv) and per-query (dq) loops in float32.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -39,7 +45,7 @@ constexpr int BWD_BM = 64;   // queries per step
 constexpr int BWD_THREADS = 256;
 
 // --------------------------------------------------------------------------
-// delta = rowsum(dout * out) (float32), and dq_acc := 0 when present.
+// delta = rowsum(dout * out), lse2 = lse * log2(e) (float32), dq_acc := 0.
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
@@ -76,12 +82,14 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
   if (row < rows && c == 0) {
-    // row = (b * T + t) * H + h  ->  delta[b, h, t]
+    // row = (b * T + t) * H + h  ->  [b, h, t]
     const long bt = row / p.H;
     const int h = (int)(row - bt * p.H);
     const long b = bt / p.T;
     const int t = (int)(bt - b * p.T);
-    p.delta[((size_t)b * p.H + h) * p.T + t] = acc;
+    const size_t o = ((size_t)b * p.H + h) * p.T + t;
+    p.delta[o] = acc;
+    p.lse2[o] = p.lse[o] * kLog2e;
   }
 }
 
@@ -103,15 +111,18 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
   constexpr int NCS = BWD_BM / 8;  // chunks per row of the dS^T tile [key][query]
   constexpr int NS = D / 16;
   constexpr int ND = D / 32;
-  constexpr int QLOADS = BWD_BM * NC / BWD_THREADS;
-  constexpr int KLOADS = BWD_BN * NC / BWD_THREADS;
-  static_assert(QLOADS >= 1 && KLOADS >= 1, "tile/thread mismatch");
-  __shared__ __attribute__((aligned(16))) unsigned short k_lds[BWD_BN * D];
-  __shared__ __attribute__((aligned(16))) unsigned short q_lds[BWD_BM * D];
-  __shared__ __attribute__((aligned(16))) unsigned short do_lds[BWD_BM * D];
+  constexpr int QT = BWD_BM * D;   // elements of one q or dO tile
+  constexpr int RPI = 64 / NC;     // tile rows per direct-to-LDS instruction
+  constexpr int QIPW = BWD_BM / RPI / 4;   // such instructions per wave per tensor
+  constexpr int KIPW = BWD_BN / RPI / 4;
+  static_assert(QIPW >= 1 && KIPW >= 1, "tile/wave mismatch");
+  static_assert(2 * QT >= BWD_BN * D, "K staging must fit in the q tile buffers");
+  // q/dO tiles double-buffered; the K tile is staged once in q_lds at start
+  __shared__ __attribute__((aligned(16))) unsigned short q_lds[2][QT];
+  __shared__ __attribute__((aligned(16))) unsigned short do_lds[2][QT];
   __shared__ __attribute__((aligned(16))) unsigned short ds_lds[BWD_BN * BWD_BM];
-  __shared__ float lse2_lds[BWD_BM];
-  __shared__ float delta_lds[BWD_BM];
+  __shared__ __attribute__((aligned(16))) float lse2_lds[2][BWD_BM];
+  __shared__ __attribute__((aligned(16))) float dl_lds[2][BWD_BM];
 
   const int T = p.T;
   const int nkt = (T + BWD_BN - 1) / BWD_BN;
@@ -123,27 +134,32 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
   const int G = p.H / p.Hkv;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hh = lane >> 5;
   const int grp = lane >> 4, t16 = lane & 15;
   const int j0 = kt * BWD_BN;
   const int kw = j0 + wave * 32;
   const int kj = kw + li;  // this lane's key
 
-  const size_t qrs = (size_t)p.H * D;
-  const size_t kvrs = (size_t)p.Hkv * D;
+  const unsigned qrs = (unsigned)(p.H * D);
+  const unsigned kvrs = (unsigned)(p.Hkv * D);
   const unsigned short* kp = (const unsigned short*)p.k + (size_t)b * T * kvrs + (size_t)g * D;
   const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * T * kvrs + (size_t)g * D;
 
-  // K tile -> LDS (B operand of dQ = dS K via transpose reads).
+  // ---- K tile -> LDS (rows past T clamped), then K^T fragments for dQ ----
+  // This wave forms dQ for d in [32 dbw, 32 dbw + 32); ktf[u] holds the B
+  // operand K[16 u + 8 hh + e][32 dbw + li] for the 16-key step u.
+  const int dbw = wave % ND;
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)(((size_t)(T - 1) * kvrs + D) * 2));
 #pragma unroll
-  for (int n = 0; n < KLOADS; ++n) {
-    const int c = tid + n * BWD_THREADS;
-    const int row = c / NC, ch = c - row * NC;
-    const int j = j0 + row;
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (j < T) w = *(const u32x4*)(kp + (size_t)j * kvrs + ch * 8);
-    *(u32x4*)(k_lds + swz_off<NC>(row, ch * 8)) = w;
+    for (int n = 0; n < KIPW; ++n) {
+      const int inst = wave * KIPW + n;
+      const int row = inst * RPI + lane / NC;
+      const int ch = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
+      const int j = min(j0 + row, T - 1);
+      buf2lds16(krs, (unsigned)(j * kvrs + ch * 8) * 2u, 0u, &q_lds[0][inst * RPI * D]);
+    }
   }
   // K and V fragments of this lane's key: lane (li, hh) holds x[kj][16 s + 8 hh + e].
   bf16x8 kf[NS], vf[NS];
@@ -157,6 +173,22 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
     kf[s] = __builtin_bit_cast(bf16x8, a);
     vf[s] = __builtin_bit_cast(bf16x8, c);
   }
+  const int tr_row = t16 >> 2;
+  const int tr_col = 16 * (grp & 1) + 4 * (t16 & 3);
+  wait_vmem();
+  __syncthreads();
+  bf16x8 ktf[BWD_BN / 16];
+  {
+    const unsigned short* kl = q_lds[0];
+#pragma unroll
+    for (int u = 0; u < BWD_BN / 16; ++u) {
+      const int r0 = 16 * u + 8 * hh + tr_row;
+      const s16x4 b1 = lds_read_tr16(kl + swz_off<NC>(r0, 32 * dbw + tr_col));
+      const s16x4 b2 = lds_read_tr16(kl + swz_off<NC>(r0 + 4, 32 * dbw + tr_col));
+      ktf[u] = cat_bf16x8(b1, b2);
+    }
+  }
+  __syncthreads();  // every wave has its K^T fragments before q/dO tiles overwrite the staging area
 
   f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -167,143 +199,207 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
 
   const bool full = p.window <= 0;
   const int win = p.window;
+  const unsigned wlim = full ? 0x80000000u : (unsigned)win;
   const int i_last = full ? T - 1 : min(T - 1, j0 + BWD_BN - 1 + win - 1);
   const int it_begin = j0 / BWD_BM, n_it = i_last / BWD_BM - it_begin + 1;
   const int n_steps = G * n_it;
-  const int tr_row = t16 >> 2;
-  const int tr_col = 16 * (grp & 1) + 4 * (t16 & 3);
 
-  // Registers holding the next step's q/dO tile rows, lse and delta.
-  u32x4 qreg[QLOADS], oreg[QLOADS];
-  float lreg = INFINITY, dreg = 0.f;
-  auto prefetch = [&](int step) {
+  // ---- per-lane constant LDS offsets ----
+  // q/dO operand rows li (+32 ib) at chunk 2 st + hh
+  int aoff[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) aoff[st] = swz_off<NC>(li, 16 * st + 8 * hh);
+  // transpose reads of dO^T / Q^T: rows 4 hh + t16/4 (+8) (+16 u + 32 ib), columns 32 d + tr_col
+  int toff1[ND], toff2[ND];
+#pragma unroll
+  for (int d = 0; d < ND; ++d) {
+    toff1[d] = swz_off<NC>(4 * hh + tr_row, 32 * d + tr_col);
+    toff2[d] = swz_off<NC>(4 * hh + tr_row + 8, 32 * d + tr_col);
+  }
+  // dS^T transpose reads for dQ: rows 16 u + 8 hh + t16/4 (+4), columns 32 ib + tr_col
+  int soff1[2], soff2[2];
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib) {
+    soff1[ib] = swz_off<NCS>(8 * hh + tr_row, 32 * ib + tr_col);
+    soff2[ib] = swz_off<NCS>(8 * hh + tr_row + 4, 32 * ib + tr_col);
+  }
+  // dS^T stores: row wave*32 + li, columns 32 ib + 8 rg + 4 hh
+  int woff[2][4];
+#pragma unroll
+  for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) woff[ib][rg] = swz_off<NCS>(wave * 32 + li, 32 * ib + 8 * rg + 4 * hh);
+
+  // ---- q/dO tile loads (buffer -> LDS) ----
+  unsigned ld_off[QIPW];
+  int ld_row[QIPW], ld_ch[QIPW];
+#pragma unroll
+  for (int n = 0; n < QIPW; ++n) {
+    const int row = (wave * QIPW + n) * RPI + lane / NC;
+    ld_row[n] = row;
+    ld_ch[n] = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
+    ld_off[n] = (unsigned)(row * qrs + ld_ch[n] * 8) * 2u;
+  }
+  const unsigned qspan = (unsigned)(((size_t)(T - 1) * qrs + D) * 2);
+  auto issue_step = [&](int step, int buf) {
     const int hq = step / n_it;
     const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
     const int h = g * G + hq;
     const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
     const unsigned short* dop = (const unsigned short*)p.dout + (size_t)b * T * qrs + (size_t)h * D;
+    const __amdgpu_buffer_rsrc_t qrsr = make_rsrc(qp, qspan), orsr = make_rsrc(dop, qspan);
+    if (i0 + BWD_BM <= T) {
+      const unsigned so = (unsigned)i0 * qrs * 2u;
 #pragma unroll
-    for (int n = 0; n < QLOADS; ++n) {
-      const int c = tid + n * BWD_THREADS;
-      const int row = c / NC, ch = c - row * NC;
-      const int i = i0 + row;
-      qreg[n] = (u32x4){0u, 0u, 0u, 0u};
-      oreg[n] = (u32x4){0u, 0u, 0u, 0u};
-      if (i < T) {
-        qreg[n] = *(const u32x4*)(qp + (size_t)i * qrs + ch * 8);
-        oreg[n] = *(const u32x4*)(dop + (size_t)i * qrs + ch * 8);
+      for (int n = 0; n < QIPW; ++n) {
+        buf2lds16(qrsr, ld_off[n], so, &q_lds[buf][(wave * QIPW + n) * RPI * D]);
+        buf2lds16(orsr, ld_off[n], so, &do_lds[buf][(wave * QIPW + n) * RPI * D]);
+      }
+    } else {
+#pragma unroll
+      for (int n = 0; n < QIPW; ++n) {
+        const int i = min(i0 + ld_row[n], T - 1);
+        const unsigned vo = (unsigned)(i * qrs + ld_ch[n] * 8) * 2u;
+        buf2lds16(qrsr, vo, 0u, &q_lds[buf][(wave * QIPW + n) * RPI * D]);
+        buf2lds16(orsr, vo, 0u, &do_lds[buf][(wave * QIPW + n) * RPI * D]);
       }
     }
-    if (tid < BWD_BM) {
-      const int i = i0 + tid;
-      const size_t li2 = ((size_t)b * p.H + h) * T + i;
-      lreg = i < T ? p.lse[li2] * kLog2e : INFINITY;
-      dreg = i < T ? p.delta[li2] : 0.f;
+    if (wave < 2) {  // per-row statistics: wave 0 lse2, wave 1 delta (rows past T clamped)
+      const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + h) * T;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (unsigned)T * 4u);
+      const int i = min(i0 + lane, T - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)((size_t)(wave == 0 ? lse2_lds[buf] : dl_lds[buf])), 4,
+          (unsigned)i * 4u, 0u, 0, 0);
     }
   };
 
-  prefetch(0);
-  for (int step = 0; step < n_steps; ++step) {
+  // dQ accumulator rows (buffer atomics): voffset per (ib), soffset per (step, r)
+  const int n_qb = (2 * ND + 3 - wave) / 4;  // dQ blocks of this wave: n = wave + 4 m < 2 ND
+  const int ib_first = wave / ND;            // ib of block m is ib_first + m (ND = 4: 0, 1)
+
+  // The dQ atomics of a step stay in flight into the next step: the wait at
+  // the top of a step only covers the loads issued before those atomics
+  // (vector memory operations complete in issue order).
+  int pending = 0;  // atomic instructions this wave issued after the last tile load
+  issue_step(0, 0);
+  auto step_fn = [&](int step, auto bufc) {
+    constexpr int buf = decltype(bufc)::value;
     const int hq = step / n_it;
     const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
     const int h = g * G + hq;
-    __syncthreads();  // every reader of the previous step's tiles is done
-#pragma unroll
-    for (int n = 0; n < QLOADS; ++n) {
-      const int c = tid + n * BWD_THREADS;
-      const int row = c / NC, ch = c - row * NC;
-      *(u32x4*)(q_lds + swz_off<NC>(row, ch * 8)) = qreg[n];
-      *(u32x4*)(do_lds + swz_off<NC>(row, ch * 8)) = oreg[n];
-    }
-    if (tid < BWD_BM) {
-      lse2_lds[tid] = lreg;
-      delta_lds[tid] = dreg;
-    }
-    __syncthreads();
-    if (step + 1 < n_steps) prefetch(step + 1);
+    wait_vmem_leq(pending);
+    __syncthreads();  // step's tiles landed; previous dQ readers are done with ds_lds
+    if (step + 1 < n_steps) issue_step(step + 1, buf ^ 1);
+    const unsigned short* ql = q_lds[buf];
+    const unsigned short* ol = do_lds[buf];
 
     const bool any = (kw <= i0 + BWD_BM - 1) && (full || kw + 31 > i0 - win);
-    const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win);
+    const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win) && (i0 + BWD_BM <= T);
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
-      float dsr[16];
+      unsigned pw[8], sw[8];  // P and dS as bf16 pairs
       if (any) {
         f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          const bf16x8 aq = *(const bf16x8*)(q_lds + swz_off<NC>(32 * ib + li, 16 * st + 8 * hh));
+          const bf16x8 aq = *(const bf16x8*)(ql + aoff[st] + 32 * ib * D);
+          const bf16x8 ad = *(const bf16x8*)(ol + aoff[st] + 32 * ib * D);
           sacc = mfma32(aq, kf[st], sacc);
-          const bf16x8 ad = *(const bf16x8*)(do_lds + swz_off<NC>(32 * ib + li, 16 * st + 8 * hh));
           dpacc = mfma32(ad, vf[st], dpacc);
         }
         // sacc[r] = S[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][key kj]
-        float pr[16];
+        const int mbase = i0 + 32 * ib + 4 * hh - kj;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int il = 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3);
-          float pv = exp2_fast(fmaf(sacc[r], p.scale_log2, -lse2_lds[il]));
-          if (!interior) {
-            const int i = i0 + il;
-            const bool vis = (kj <= i) && (full || kj > i - win);
-            if (!vis) pv = 0.f;
+        for (int rg = 0; rg < 4; ++rg) {
+          const f32x4 l4 = *(const f32x4*)(&lse2_lds[buf][32 * ib + 8 * rg + 4 * hh]);
+          const f32x4 d4 = *(const f32x4*)(&dl_lds[buf][32 * ib + 8 * rg + 4 * hh]);
+          float pr[4], dsr[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rg + e;
+            float pv = exp2_fast(fmaf(sacc[r], p.scale_log2, -l4[e]));
+            if (!interior) {
+              const int off = 8 * rg + e;
+              const bool vis = ((unsigned)(mbase + off) < wlim) && (i0 + 32 * ib + 8 * rg + 4 * hh + e < T);
+              if (!vis) pv = 0.f;
+            }
+            pr[e] = pv;
+            dsr[e] = pv * (dpacc[r] - d4[e]);
           }
-          pr[r] = pv;
-          dsr[r] = pv * (dpacc[r] - delta_lds[il]);
+          pw[2 * rg] = pk_bf16(pr[0], pr[1]);
+          pw[2 * rg + 1] = pk_bf16(pr[2], pr[3]);
+          sw[2 * rg] = pk_bf16(dsr[0], dsr[1]);
+          sw[2 * rg + 1] = pk_bf16(dsr[2], dsr[3]);
         }
         // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const bf16x8 pb = to_bf16x8(&pr[8 * u]);
-          const bf16x8 sb = to_bf16x8(&dsr[8 * u]);
-          const int r1 = 32 * ib + 16 * u + 4 * hh + tr_row;
+          const u32x4 pq = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+          const u32x4 sq = {sw[4 * u], sw[4 * u + 1], sw[4 * u + 2], sw[4 * u + 3]};
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pq);
+          const bf16x8 sb = __builtin_bit_cast(bf16x8, sq);
+          const int rb = (32 * ib + 16 * u) * D;
 #pragma unroll
           for (int d = 0; d < ND; ++d) {
-            const int col = 32 * d + tr_col;
-            const s16x4 o1 = lds_read_tr16(do_lds + swz_off<NC>(r1, col));
-            const s16x4 o2 = lds_read_tr16(do_lds + swz_off<NC>(r1 + 8, col));
+            const s16x4 o1 = lds_read_tr16(ol + toff1[d] + rb);
+            const s16x4 o2 = lds_read_tr16(ol + toff2[d] + rb);
+            const s16x4 q1 = lds_read_tr16(ql + toff1[d] + rb);
+            const s16x4 q2 = lds_read_tr16(ql + toff2[d] + rb);
             dv[d] = mfma32(cat_bf16x8(o1, o2), pb, dv[d]);
-            const s16x4 q1 = lds_read_tr16(q_lds + swz_off<NC>(r1, col));
-            const s16x4 q2 = lds_read_tr16(q_lds + swz_off<NC>(r1 + 8, col));
             dk[d] = mfma32(cat_bf16x8(q1, q2), sb, dk[d]);
           }
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dsr[r] = 0.f;
+        for (int i = 0; i < 8; ++i) sw[i] = 0u;
       }
       // dS^T -> LDS: row = key (wave*32 + li), 4 consecutive queries per store.
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        u32x2 w;
-        w[0] = pack2_bf16(dsr[4 * rg], dsr[4 * rg + 1]);
-        w[1] = pack2_bf16(dsr[4 * rg + 2], dsr[4 * rg + 3]);
-        *(u32x2*)(ds_lds + swz_off<NCS>(wave * 32 + li, 32 * ib + 8 * rg + 4 * hh)) = w;
-      }
+      for (int rg = 0; rg < 4; ++rg) *(u32x2*)(ds_lds + woff[ib][rg]) = (u32x2){sw[2 * rg], sw[2 * rg + 1]};
     }
     __syncthreads();
 
-    // dQ[i][d] = sum over the 128 keys of dS[i][j] K[j][d]; output blocks
-    // (ib, db) are dealt to the waves.
+    // dQ[i][d] = sum over the 128 keys of dS[i][j] K[j][d] for this wave's
+    // d slice; added to the float32 accumulator rows i0 .. i0+63 of head h.
     float* dqa = p.dq_acc + (size_t)b * T * qrs + (size_t)h * D;
-    for (int n = wave; n < 2 * ND; n += 4) {
-      const int ib = n / ND, db = n - (n / ND) * ND;
+    const __amdgpu_buffer_rsrc_t dqr = make_rsrc(dqa, (unsigned)((size_t)T * qrs * 4));
+    pending = 0;
+    for (int m = 0; m < n_qb; ++m) {
+      const int ib = ib_first + m;
       f32x16 acc = (f32x16){};
 #pragma unroll
       for (int u = 0; u < BWD_BN / 16; ++u) {
-        const int r0 = 16 * u + 8 * hh + tr_row;
-        const s16x4 a1 = lds_read_tr16(ds_lds + swz_off<NCS>(r0, 32 * ib + tr_col));
-        const s16x4 a2 = lds_read_tr16(ds_lds + swz_off<NCS>(r0 + 4, 32 * ib + tr_col));
-        const s16x4 b1 = lds_read_tr16(k_lds + swz_off<NC>(r0, 32 * db + tr_col));
-        const s16x4 b2 = lds_read_tr16(k_lds + swz_off<NC>(r0 + 4, 32 * db + tr_col));
-        acc = mfma32(cat_bf16x8(a1, a2), cat_bf16x8(b1, b2), acc);
+        const int rb = 16 * u * BWD_BM;
+        const s16x4 a1 = lds_read_tr16(ds_lds + (ib ? soff1[1] : soff1[0]) + rb);
+        const s16x4 a2 = lds_read_tr16(ds_lds + (ib ? soff2[1] : soff2[0]) + rb);
+        acc = mfma32(cat_bf16x8(a1, a2), ktf[u], acc);
       }
-      // acc[r] = dQ[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][d = 32 db + li]
+      // acc[r] = dQ[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][d = 32 dbw + li]
+      const unsigned vo = (unsigned)((32 * ib + 4 * hh) * qrs + 32 * dbw + li) * 4u;
+      if (i0 + BWD_BM <= T) {
+        pending += 16;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = i0 + 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3);
-        if (i < T) atomicAdd(dqa + (size_t)i * qrs + 32 * db + li, acc[r] * p.scale);
+        for (int r = 0; r < 16; ++r) {
+          const unsigned so = (unsigned)(i0 + 8 * (r >> 2) + (r & 3)) * qrs * 4u;
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * p.scale, dqr, vo, so, 0);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = i0 + 32 * ib + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (i < T) {
+            const unsigned so = (unsigned)(i0 + 8 * (r >> 2) + (r & 3)) * qrs * 4u;
+            __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[r] * p.scale, dqr, vo, so, 0);
+          }
+        }
       }
     }
+  };
+
+  for (int step = 0; step < n_steps; step += 2) {
+    step_fn(step, std::integral_constant<int, 0>{});
+    if (step + 1 < n_steps) step_fn(step + 1, std::integral_constant<int, 1>{});
   }
 
   // dK (scaled) and dV for this lane's key.
@@ -315,10 +411,10 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         u32x2 wk, wv;
-        wk[0] = pack2_bf16(dk[d][4 * rg] * p.scale, dk[d][4 * rg + 1] * p.scale);
-        wk[1] = pack2_bf16(dk[d][4 * rg + 2] * p.scale, dk[d][4 * rg + 3] * p.scale);
-        wv[0] = pack2_bf16(dv[d][4 * rg], dv[d][4 * rg + 1]);
-        wv[1] = pack2_bf16(dv[d][4 * rg + 2], dv[d][4 * rg + 3]);
+        wk[0] = pk_bf16(dk[d][4 * rg] * p.scale, dk[d][4 * rg + 1] * p.scale);
+        wk[1] = pk_bf16(dk[d][4 * rg + 2] * p.scale, dk[d][4 * rg + 3] * p.scale);
+        wv[0] = pk_bf16(dv[d][4 * rg], dv[d][4 * rg + 1]);
+        wv[1] = pk_bf16(dv[d][4 * rg + 2], dv[d][4 * rg + 3]);
         *(u32x2*)(dkp + 32 * d + 8 * rg + 4 * hh) = wk;
         *(u32x2*)(dvp + 32 * d + 8 * rg + 4 * hh) = wv;
       }
@@ -414,6 +510,7 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdParams p) {
 #pragma unroll
   for (int d = 0; d < D; ++d) dqp[d] = dq[d] * p.scale;
 }
+
 
 template <int D, bool BF16>
 hipError_t launch_pre(const BwdParams& p, hipStream_t s) {

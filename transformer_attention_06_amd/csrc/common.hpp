@@ -91,6 +91,16 @@ __device__ __forceinline__ float add2_bf16(unsigned w, float c) {
 
 // Wait until all of this wave's global loads (including direct-to-LDS ones) completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// Wait until at most n (rounded down to 0, 16 or 32; n wave-uniform) of this
+// wave's vector memory operations are outstanding.
+__device__ __forceinline__ void wait_vmem_leq(int n) {
+  if (n >= 32)
+    __builtin_amdgcn_s_waitcnt(0x8f70);  // vmcnt(32)
+  else if (n >= 16)
+    __builtin_amdgcn_s_waitcnt(0x4f70);  // vmcnt(16)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+}
 
 // ---------------------------------------------------------------------------
 // Exponentials: v_exp_f32 computes 2^x; callers fold log2(e) into their scale.

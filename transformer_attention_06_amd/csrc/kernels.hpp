@@ -30,6 +30,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* delta;   // [B, H, T] workspace
+  float* lse2;    // [B, H, T] workspace: lse * log2(e)
   float* dq_acc;  // [B, T, H, D] workspace
   int B, T, H, Hkv, D;
   int window;
