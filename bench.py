@@ -29,8 +29,29 @@ PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd+bwd TFLOP/s (band-counted) at d20 T=2048; decode GB/s"
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic(label):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (profiles/attn_d20_traffic.json: FETCH_SIZE and WRITE_SIZE, each
+    scaled by a plain-copy calibration), or None when there is no summary for
+    it or its source file has changed since the counters were taken."""
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "profiles", "attn_d20_traffic.json")) as f:
+            d = json.load(f)[label]
+        with open(os.path.join(ROOT, d["source"]), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != d["source_sha256"]:
+                return None
+        return {"bytes": round(d["fetch_bytes_per_launch"] + d["write_bytes_per_launch"]),
+                "read": round(d["fetch_bytes_per_launch"]), "written": round(d["write_bytes_per_launch"])}
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -219,9 +240,11 @@ def main():
     dom_flops = flops_f if dom == "attn_fwd" else flops_b
     n_launch = kern[dom]["launches_per_step"]
     achieved = dom_flops / n_launch / (kern[dom]["avg_ms_per_launch"] * 1e-3) / 1e12
+    tr = measured_traffic(dom)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None,
+                "traffic": tr["bytes"] if tr else None,
+                "traffic_split": tr,
                 "note": "achieved = band-counted flops per launch (8*D or 4*D per visible pair, "
                         "B*H*pairs(T,w) pairs) / average launch time, averaged over the 20 layers"}
 
