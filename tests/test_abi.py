@@ -117,8 +117,11 @@ def test_bwd_validation(L):
 
 
 def test_decode_workspace_query_is_pure(L):
-    assert L.nc_attn_decode_workspace_bytes(BF16, 64, 10, 10, 128, 2048) == 64 * 10 * 8 * 130 * 4
+    # one partial of D + 2 floats per (row, query head, chunk); a chunk is
+    # (64 / (D/8)) lane groups x 16, 8 or 4 positions for G <= 2, <= 4, <= 8
+    assert L.nc_attn_decode_workspace_bytes(BF16, 64, 10, 10, 128, 2048) == 64 * 10 * 32 * 130 * 4
     assert L.nc_attn_decode_workspace_bytes(BF16, 3, 4, 2, 32, 257) == 3 * 4 * 2 * 34 * 4
+    assert L.nc_attn_decode_workspace_bytes(BF16, 3, 8, 2, 64, 100) == 3 * 8 * 2 * 66 * 4
     assert L.nc_attn_decode_workspace_bytes(BF16, 3, 4, 3, 32, 257) == 0
 
 

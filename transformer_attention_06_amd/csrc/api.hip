@@ -108,7 +108,10 @@ nc_status finish(hipError_t e, hipStream_t s, const char* what) {
 
 int norm_window(int window, int T) { return (window <= 0 || window >= T) ? 0 : window; }
 
-int decode_splits(int T_max) { return (T_max + nc::kDecodeSplit - 1) / nc::kDecodeSplit; }
+int decode_splits(int T_max, int D, int G) {
+  const int chunk = nc::decode_chunk(D, G);
+  return (T_max + chunk - 1) / chunk;
+}
 
 }  // namespace
 
@@ -194,7 +197,7 @@ nc_status nc_profile_bwd_main(void* begin_event, void* end_event) {
 
 size_t nc_attn_decode_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, int D, int T_max) {
   if (check_shape(dt, B, T_max, H, Hkv, D) != NC_OK) return 0;
-  return (size_t)B * H * decode_splits(T_max) * (D + 2) * 4;
+  return (size_t)B * H * decode_splits(T_max, D, H / Hkv) * (D + 2) * 4;
 }
 
 nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q,
@@ -220,7 +223,7 @@ nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, c
     return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   NC_TRY(check_device(nullptr));
   nc::DecodeParams p{q, k_cache, v_cache, seqlens, out, lse, (float*)workspace, B, H, Hkv, D, T_max,
-                     window <= 0 ? 0 : window, decode_splits(T_max), scale, scale * 1.4426950408889634f};
+                     window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), scale, scale * 1.4426950408889634f};
   hipStream_t s = (hipStream_t)stream;
   return finish(nc::launch_decode(p, dt == NC_BF16, s), s, "nc_attn_decode");
 }

@@ -110,6 +110,23 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // Cross-lane helpers (wave64).
 __device__ __forceinline__ float shfl_xor(float x, int mask) { return __shfl_xor(x, mask, 64); }
 
+// Sum over each aligned group of N lanes (N = 2, 4, 8 or 16), result in every
+// lane of the group, with DPP moves inside 16-lane rows (no LDS traffic):
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group of 2..16 lanes");
+  x += dpp_mov<0xB1>(x);                // quad_perm [1,0,3,2]
+  if (N >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]
+  if (N >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror
+  if (N >= 16) x += dpp_mov<0x140>(x);  // row_mirror
+  return x;
+}
+
 // ---------------------------------------------------------------------------
 // LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane t supplies the address of 4 consecutive 16-bit elements; the result

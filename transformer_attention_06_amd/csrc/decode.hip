@@ -7,16 +7,17 @@
 // (B, T, H, D) cache, per-row int32 lengths; section 6: single-token decode
 // slices the key window.)
 //
-// decode_split: one workgroup per (split of 256 cache positions, kv head,
-//   row). Each group of D/8 lanes streams one cache row at a time (D/8 lanes
-//   x 16 bytes = the contiguous head vector), so a wave reads whole 256-byte
-//   rows; the dot product is finished with a butterfly of cross-lane
-//   exchanges inside the group. Each group keeps an online softmax
-//   (m, l, acc) per query head of the GQA group; the groups are merged in
-//   LDS and one partial per (row, head, split) goes to the workspace.
-//   Splits outside a row's key range exit without reading anything.
-// decode_combine: merges a row's partials into out and lse. A length
-//   outside 1..T_max yields NaN out and lse for that row.
+// decode_split: one wave per (chunk of cache positions, kv head, row). The
+//   wave's groups of D/8 lanes each take every NGR-th position of the chunk,
+//   so one load instruction reads NGR whole head vectors (256 bytes each at
+//   D = 128). All of a group's K and V rows are requested before any is used
+//   (one memory round trip per wave), the dot products are finished with DPP
+//   exchanges inside the group, the softmax is taken in one pass over the
+//   known scores, and the groups are merged with cross-row exchanges. One
+//   partial (acc[D], m, l) per (row, query head, chunk) goes to the workspace.
+//   Chunks outside a row's key range exit without reading anything.
+// decode_combine: merges a row's partials into out and lse. A length outside
+//   1..T_max yields NaN out and lse for that row.
 
 #include <math.h>
 
@@ -26,16 +27,29 @@
 namespace nc {
 namespace {
 
-constexpr int DEC_THREADS = 256;
-constexpr int DEC_KU = 4;  // cache rows in flight per group
-
+// 8 elements of a cache row as loaded (bf16: 16 bytes, float32: 32 bytes)
 template <bool BF16>
-__device__ __forceinline__ void load8(const void* base, size_t elem_off, float* f) {
+struct Raw8 {
+  u32x4 w[BF16 ? 1 : 2];
+};
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> load_raw8(const void* base, size_t elem_off) {
+  Raw8<BF16> r;
   if (BF16) {
-    unpack8_bf16(__builtin_nontemporal_load((const u32x4*)((const unsigned short*)base + elem_off)), f);
+    r.w[0] = __builtin_nontemporal_load((const u32x4*)((const unsigned short*)base + elem_off));
   } else {
-    const f32x4* p = (const f32x4*)((const float*)base + elem_off);
-    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    const u32x4* p = (const u32x4*)((const float*)base + elem_off);
+    r.w[0] = __builtin_nontemporal_load(p);
+    r.w[BF16 ? 0 : 1] = __builtin_nontemporal_load(p + 1);
+  }
+  return r;
+}
+template <bool BF16>
+__device__ __forceinline__ void unpack_raw8(const Raw8<BF16>& r, float* f) {
+  if (BF16) {
+    unpack8_bf16(r.w[0], f);
+  } else {
+    const f32x4 a = __builtin_bit_cast(f32x4, r.w[0]), b = __builtin_bit_cast(f32x4, r.w[BF16 ? 0 : 1]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[i] = a[i];
@@ -45,119 +59,113 @@ __device__ __forceinline__ void load8(const void* base, size_t elem_off, float* 
 }
 
 template <int D, int G, bool BF16>
-__global__ __launch_bounds__(DEC_THREADS) void decode_split_kernel(DecodeParams p) {
-  constexpr int LPR = D / 8;               // lanes per cache row
-  constexpr int NG = DEC_THREADS / LPR;    // row groups per workgroup
-  __shared__ float red_acc[NG * D];
-  __shared__ float red_m[NG], red_l[NG];
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
+  constexpr int LPR = D / 8;              // lanes per cache row (divides 16)
+  constexpr int NGR = 64 / LPR;           // row groups per wave
+  constexpr int KPG = decode_keys_per_group(G);
+  constexpr int CHUNK = NGR * KPG;        // positions per wave
+  static_assert(CHUNK == decode_chunk(D, G), "chunk size mismatch");
 
   const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = p.seqlens[b];
   if (L < 1 || L > p.T_max) return;
   const bool full = p.window <= 0 || p.window >= L;
   const int lo = full ? 0 : L - p.window;
-  const int k_begin = max(lo, sp * kDecodeSplit);
-  const int k_end = min(L, (sp + 1) * kDecodeSplit);  // exclusive
+  const int k_begin = max(lo, sp * CHUNK);
+  const int k_end = min(L, (sp + 1) * CHUNK);  // exclusive
   if (k_begin >= k_end) return;
 
-  const int tid = threadIdx.x;
-  const int grp = tid / LPR, c = tid - (tid / LPR) * LPR;
+  const int lane = threadIdx.x;
+  const int grp = lane / LPR, c = lane - (lane / LPR) * LPR;
   const int H = p.H;
   const size_t rs = (size_t)p.Hkv * D;  // elements per cache position
   const size_t cache_base = (size_t)b * p.T_max * rs + (size_t)g * D + c * 8;
 
-  float qf[G][8];
+  // positions sp*CHUNK + grp + NGR*u, u = 0 .. KPG-1 (only those in [k_begin, k_end))
+  const int j0 = sp * CHUNK + grp;
+  Raw8<BF16> kr[KPG], vr[KPG];
 #pragma unroll
-  for (int hq = 0; hq < G; ++hq) {
-    float t[8];
-    if (BF16)
-      unpack8_bf16(*(const u32x4*)((const unsigned short*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8), t);
-    else {
-      const f32x4* pq = (const f32x4*)((const float*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8);
-      const f32x4 a = pq[0], bq = pq[1];
-      for (int i = 0; i < 4; ++i) {
-        t[i] = a[i];
-        t[4 + i] = bq[i];
-      }
-    }
+  for (int u = 0; u < KPG; ++u) {
+    const int j = j0 + NGR * u;
+    if (j >= k_begin && j < k_end) {
+      kr[u] = load_raw8<BF16>(p.k_cache, cache_base + (size_t)j * rs);
+      vr[u] = load_raw8<BF16>(p.v_cache, cache_base + (size_t)j * rs);
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) qf[hq][e] = t[e] * p.scale_log2;
-  }
-
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int hq = 0; hq < G; ++hq) {
-    m[hq] = -INFINITY;
-    l[hq] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[hq][e] = 0.f;
-  }
-
-  for (int j = k_begin + grp; j < k_end; j += NG * DEC_KU) {
-    float kr[DEC_KU][8], vr[DEC_KU][8];
-#pragma unroll
-    for (int u = 0; u < DEC_KU; ++u) {
-      const int jj = j + u * NG;
-      if (jj < k_end) {
-        load8<BF16>(p.k_cache, cache_base + (size_t)jj * rs, kr[u]);
-        load8<BF16>(p.v_cache, cache_base + (size_t)jj * rs, vr[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < DEC_KU; ++u) {
-      const int jj = j + u * NG;
-      if (jj >= k_end) break;  // uniform across the group
-#pragma unroll
-      for (int hq = 0; hq < G; ++hq) {
-        float s = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s = fmaf(qf[hq][e], kr[u][e], s);
-#pragma unroll
-        for (int msk = LPR / 2; msk >= 1; msk >>= 1) s += shfl_xor(s, msk);
-        const float mn = fmaxf(m[hq], s);
-        const float a = exp2_fast(m[hq] - mn);
-        const float pe = exp2_fast(s - mn);
-        l[hq] = fmaf(l[hq], a, pe);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[hq][e] = fmaf(acc[hq][e], a, pe * vr[u][e]);
-        m[hq] = mn;
+      for (int i = 0; i < (BF16 ? 1 : 2); ++i) {
+        kr[u].w[i] = (u32x4){0u, 0u, 0u, 0u};
+        vr[u].w[i] = (u32x4){0u, 0u, 0u, 0u};
       }
     }
   }
 
-  // merge the groups, one query head at a time
-  float* part_row = p.part + (((size_t)b * H + g * G) * p.n_split + sp) * (D + 2);
 #pragma unroll
   for (int hq = 0; hq < G; ++hq) {
-    __syncthreads();
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red_acc[grp * D + c * 8 + e] = acc[hq][e];
-    if (c == 0) {
-      red_m[grp] = m[hq];
-      red_l[grp] = l[hq];
-    }
-    __syncthreads();
-    if (tid < D) {
-      float M = -INFINITY;
-      for (int r = 0; r < NG; ++r) M = fmaxf(M, red_m[r]);
-      float a = 0.f, z = 0.f;
-      for (int r = 0; r < NG; ++r) {
-        const float f = red_m[r] == -INFINITY ? 0.f : exp2_fast(red_m[r] - M);
-        a = fmaf(f, red_acc[r * D + tid], a);
-        z = fmaf(f, red_l[r], z);
+    float qf[8];
+    {
+      float t[8];
+      if (BF16)
+        unpack8_bf16(*(const u32x4*)((const unsigned short*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8), t);
+      else {
+        const f32x4* pq = (const f32x4*)((const float*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8);
+        const f32x4 a = pq[0], bq = pq[1];
+        for (int i = 0; i < 4; ++i) {
+          t[i] = a[i];
+          t[4 + i] = bq[i];
+        }
       }
-      float* dst = part_row + (size_t)hq * p.n_split * (D + 2);
-      dst[tid] = a;
-      if (tid == 0) {
-        dst[D] = M;
-        dst[D + 1] = z;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[e] = t[e] * p.scale_log2;
+    }
+    // scores of the group's positions (log2 units), -inf where absent
+    float s[KPG];
+    float m = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) {
+      const int j = j0 + NGR * u;
+      float kf[8];
+      unpack_raw8<BF16>(kr[u], kf);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) d = fmaf(qf[e], kf[e], d);
+      d = group_sum<LPR>(d);
+      s[u] = (j >= k_begin && j < k_end) ? d : -INFINITY;
+      m = fmaxf(m, s[u]);
+    }
+    // the wave's maximum (at least one position is present), then one pass
+#pragma unroll
+    for (int msk = LPR; msk < 64; msk <<= 1) m = fmaxf(m, shfl_xor(m, msk));
+    float l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KPG; ++u) {
+      const float pe = exp2_fast(s[u] - m);  // 0 for absent positions (their v is 0)
+      l += pe;
+      float vf[8];
+      unpack_raw8<BF16>(vr[u], vf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(pe, vf[e], acc[e]);
+    }
+#pragma unroll
+    for (int msk = LPR; msk < 64; msk <<= 1) {
+      l += shfl_xor(l, msk);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += shfl_xor(acc[e], msk);
+    }
+    if (grp == 0) {
+      float* dst = p.part + (((size_t)b * H + g * G + hq) * p.n_split + sp) * (D + 2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dst[c * 8 + e] = acc[e];
+      if (c == 0) {
+        dst[D] = m;
+        dst[D + 1] = l;
       }
     }
   }
 }
 
-template <int D, bool BF16>
+template <int D, int G, bool BF16>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
+  constexpr int CHUNK = decode_chunk(D, G);
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int L = p.seqlens[b];
   const size_t oi = ((size_t)b * p.H + h) * D + t;
@@ -171,7 +179,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
   }
   const bool full = p.window <= 0 || p.window >= L;
   const int lo = full ? 0 : L - p.window;
-  const int s0 = lo / kDecodeSplit, s1 = (L - 1) / kDecodeSplit;
+  const int s0 = lo / CHUNK, s1 = (L - 1) / CHUNK;
   const float* part = p.part + ((size_t)b * p.H + h) * p.n_split * (D + 2);
   float M = -INFINITY;
   for (int s = s0; s <= s1; ++s) M = fmaxf(M, part[(size_t)s * (D + 2) + D]);
@@ -192,10 +200,10 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
 
 template <int D, int G, bool BF16>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-  decode_split_kernel<D, G, BF16><<<dim3(p.n_split, p.Hkv, p.B), DEC_THREADS, 0, s>>>(p);
+  decode_split_kernel<D, G, BF16><<<dim3(p.n_split, p.Hkv, p.B), 64, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  decode_combine_kernel<D, BF16><<<dim3(p.H, p.B), D, 0, s>>>(p);
+  decode_combine_kernel<D, G, BF16><<<dim3(p.H, p.B), D, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -67,8 +67,11 @@ struct PrologueParams {
   float eps;
 };
 
-// Decode split size in keys (one workgroup per (b, kv head, split)).
-constexpr int kDecodeSplit = 256;
+// Decode: cache positions per group of D/8 lanes for a query group of G heads
+// (fewer when several heads share the scores' registers), and positions per
+// wave (one wave per (row, kv head, chunk)).
+constexpr int decode_keys_per_group(int G) { return G <= 2 ? 16 : (G <= 4 ? 8 : 4); }
+constexpr int decode_chunk(int D, int G) { return (64 / (D / 8)) * decode_keys_per_group(G); }
 
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const FwdParams& p, hipStream_t s);

@@ -38,6 +38,13 @@ __global__ void rope_table_kernel(int T_rope, int half, double base, float* __re
   s[i] = (float)sn;
 }
 
+// value of the lane holding the other half of the head vector (lane ^ HALF)
+template <int HALF>
+__device__ __forceinline__ float partner(float v) {
+  if (HALF == 8) return dpp_mov<0x128>(v);  // whole 16-lane row: row_ror by 8
+  return shfl_xor(v, HALF);
+}
+
 template <bool BF16>
 __device__ __forceinline__ void ld8(const void* base, size_t off, float* f) {
   if (BF16) {
@@ -112,8 +119,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
   float ss = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) ss += shfl_xor(ss, m);
+  ss = group_sum<LPR>(ss);
   const float r = sqrtf(ss * (1.0f / D) + p.eps);
   const float inv_r = 1.0f / r;
 
@@ -123,7 +129,7 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) y[e] = x[e] * inv_r;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) yp[e] = shfl_xor(y[e], HALF);
+    for (int e = 0; e < 8; ++e) yp[e] = partner<HALF>(y[e]);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       res[e] = low ? fmaf(y[e], cs[e], -yp[e] * sn[e]) : fmaf(yp[e], sn[e], y[e] * cs[e]);
@@ -131,15 +137,14 @@ __global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
     // u = R(-theta) dy: low half a' = a c + b s, high half b' = -a s + b c
     float dp[8], u[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dp[e] = shfl_xor(dy[e], HALF);
+    for (int e = 0; e < 8; ++e) dp[e] = partner<HALF>(dy[e]);
 #pragma unroll
     for (int e = 0; e < 8; ++e)
       u[e] = low ? fmaf(dy[e], cs[e], dp[e] * sn[e]) : fmaf(dy[e], cs[e], -dp[e] * sn[e]);
     float xu = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) xu = fmaf(x[e], u[e], xu);
-#pragma unroll
-    for (int m = LPR / 2; m >= 1; m >>= 1) xu += shfl_xor(xu, m);
+    xu = group_sum<LPR>(xu);
     const float k3 = xu * inv_r * inv_r * inv_r * (1.0f / D);
 #pragma unroll
     for (int e = 0; e < 8; ++e) res[e] = fmaf(u[e], inv_r, -x[e] * k3);
