@@ -43,6 +43,7 @@ namespace {
 constexpr int BWD_BN = 128;  // keys per workgroup (32 per wave)
 constexpr int BWD_BM = 64;   // queries per step
 constexpr int BWD_THREADS = 256;
+constexpr int NBUF = 3;  // q/dO tile buffers: loads run two steps ahead
 
 // --------------------------------------------------------------------------
 // delta = rowsum(dout * out), lse2 = lse * log2(e) (float32), dq_acc := 0.
@@ -118,11 +119,11 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
   static_assert(QIPW >= 1 && KIPW >= 1, "tile/wave mismatch");
   static_assert(2 * QT >= BWD_BN * D, "K staging must fit in the q tile buffers");
   // q/dO tiles double-buffered; the K tile is staged once in q_lds at start
-  __shared__ __attribute__((aligned(16))) unsigned short q_lds[2][QT];
-  __shared__ __attribute__((aligned(16))) unsigned short do_lds[2][QT];
+  __shared__ __attribute__((aligned(16))) unsigned short q_lds[NBUF][QT];
+  __shared__ __attribute__((aligned(16))) unsigned short do_lds[NBUF][QT];
   __shared__ __attribute__((aligned(16))) unsigned short ds_lds[BWD_BN * BWD_BM];
-  __shared__ __attribute__((aligned(16))) float lse2_lds[2][BWD_BM];
-  __shared__ __attribute__((aligned(16))) float dl_lds[2][BWD_BM];
+  __shared__ __attribute__((aligned(16))) float lse2_lds[NBUF][BWD_BM];
+  __shared__ __attribute__((aligned(16))) float dl_lds[NBUF][BWD_BM];
 
   const int T = p.T;
   const int nkt = (T + BWD_BN - 1) / BWD_BN;
@@ -151,14 +152,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
   // operand K[16 u + 8 hh + e][32 dbw + li] for the 16-key step u.
   const int dbw = wave % ND;
   {
-    const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, (unsigned)(((size_t)(T - 1) * kvrs + D) * 2));
+    const BufDesc krs = buf_desc(kp, (unsigned)(((size_t)(T - 1) * kvrs + D) * 2));
 #pragma unroll
     for (int n = 0; n < KIPW; ++n) {
       const int inst = wave * KIPW + n;
       const int row = inst * RPI + lane / NC;
       const int ch = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
       const int j = min(j0 + row, T - 1);
-      buf2lds16(krs, (unsigned)(j * kvrs + ch * 8) * 2u, 0u, &q_lds[0][inst * RPI * D]);
+      dma16(krs, (unsigned)(j * kvrs + ch * 8) * 2u, 0u, lds_u32(&q_lds[0][inst * RPI * D]));
     }
   }
   // K and V fragments of this lane's key: lane (li, hh) holds x[kj][16 s + 8 hh + e].
@@ -176,7 +177,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
   const int tr_row = t16 >> 2;
   const int tr_col = 16 * (grp & 1) + 4 * (t16 & 3);
   wait_vmem();
-  __syncthreads();
+  lds_barrier();
   bf16x8 ktf[BWD_BN / 16];
   {
     const unsigned short* kl = q_lds[0];
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
       ktf[u] = cat_bf16x8(b1, b2);
     }
   }
-  __syncthreads();  // every wave has its K^T fragments before q/dO tiles overwrite the staging area
+  lds_barrier();  // every wave has its K^T fragments before q/dO tiles overwrite the staging area
 
   f32x16 dk[ND], dv[ND];
 #pragma unroll
@@ -247,30 +248,27 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
     const int h = g * G + hq;
     const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
     const unsigned short* dop = (const unsigned short*)p.dout + (size_t)b * T * qrs + (size_t)h * D;
-    const __amdgpu_buffer_rsrc_t qrsr = make_rsrc(qp, qspan), orsr = make_rsrc(dop, qspan);
+    const BufDesc qrsr = buf_desc(qp, qspan), orsr = buf_desc(dop, qspan);
     if (i0 + BWD_BM <= T) {
       const unsigned so = (unsigned)i0 * qrs * 2u;
 #pragma unroll
       for (int n = 0; n < QIPW; ++n) {
-        buf2lds16(qrsr, ld_off[n], so, &q_lds[buf][(wave * QIPW + n) * RPI * D]);
-        buf2lds16(orsr, ld_off[n], so, &do_lds[buf][(wave * QIPW + n) * RPI * D]);
+        dma16(qrsr, ld_off[n], so, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
+        dma16(orsr, ld_off[n], so, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
       }
     } else {
 #pragma unroll
       for (int n = 0; n < QIPW; ++n) {
         const int i = min(i0 + ld_row[n], T - 1);
         const unsigned vo = (unsigned)(i * qrs + ld_ch[n] * 8) * 2u;
-        buf2lds16(qrsr, vo, 0u, &q_lds[buf][(wave * QIPW + n) * RPI * D]);
-        buf2lds16(orsr, vo, 0u, &do_lds[buf][(wave * QIPW + n) * RPI * D]);
+        dma16(qrsr, vo, 0u, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
+        dma16(orsr, vo, 0u, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
       }
     }
     if (wave < 2) {  // per-row statistics: wave 0 lse2, wave 1 delta (rows past T clamped)
       const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + h) * T;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (unsigned)T * 4u);
       const int i = min(i0 + lane, T - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)((size_t)(wave == 0 ? lse2_lds[buf] : dl_lds[buf])), 4,
-          (unsigned)i * 4u, 0u, 0, 0);
+      dma4(buf_desc(src, (unsigned)T * 4u), (unsigned)i * 4u, 0u, lds_u32(wave == 0 ? lse2_lds[buf] : dl_lds[buf]));
     }
   };
 
@@ -281,16 +279,23 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
   // The dQ atomics of a step stay in flight into the next step: the wait at
   // the top of a step only covers the loads issued before those atomics
   // (vector memory operations complete in issue order).
-  int pending = 0;  // atomic instructions this wave issued after the last tile load
+  // Vector memory operations complete in issue order, so the wait at the top
+  // of step t only has to cover the tile loads of step t: the loads of step
+  // t+1 and the dQ atomics of steps t-2 and t-1, issued after them, may stay
+  // in flight.
+  const int dma_ops = 2 * QIPW + (wave < 2 ? 1 : 0);  // loads this wave issues per step
+  int at_prev2 = 0, at_prev1 = 0;                     // atomics of steps t-2, t-1
+  int pending = 0;                                    // atomics of the current step (0 if unknown)
   issue_step(0, 0);
+  if (n_steps > 1) issue_step(1, 1);
   auto step_fn = [&](int step, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
     const int hq = step / n_it;
     const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
     const int h = g * G + hq;
-    wait_vmem_leq(pending);
-    __syncthreads();  // step's tiles landed; previous dQ readers are done with ds_lds
-    if (step + 1 < n_steps) issue_step(step + 1, buf ^ 1);
+    wait_vmem_upto(at_prev2 + at_prev1 + (step + 1 < n_steps ? dma_ops : 0));
+    lds_barrier();  // step's tiles landed; previous dQ readers are done with ds_lds
+    if (step + 2 < n_steps) issue_step(step + 2, (buf + 2) % NBUF);
     const unsigned short* ql = q_lds[buf];
     const unsigned short* ol = do_lds[buf];
 
@@ -298,40 +303,69 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
     const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win) && (i0 + BWD_BM <= T);
 #pragma unroll
     for (int ib = 0; ib < 2; ++ib) {
-      unsigned pw[8], sw[8];  // P and dS as bf16 pairs
+      unsigned sw[8];  // dS as bf16 pairs
       if (any) {
+        // Every LDS operand of this 32-query half is requested before the
+        // first product: q and dO rows (S, dP), the row statistics, and the
+        // dO^T / Q^T transpose reads (dV, dK).
+        bf16x8 aq[NS], ad[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          aq[st] = *(const bf16x8*)(ql + aoff[st] + 32 * ib * D);
+          ad[st] = *(const bf16x8*)(ol + aoff[st] + 32 * ib * D);
+        }
+        f32x4 l4[4], d4[4];
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          l4[rg] = *(const f32x4*)(&lse2_lds[buf][32 * ib + 8 * rg + 4 * hh]);
+          d4[rg] = *(const f32x4*)(&dl_lds[buf][32 * ib + 8 * rg + 4 * hh]);
+        }
+        bf16x8 ot[2][ND], qt[2][ND];
+#pragma unroll
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            const int rb = (32 * ib + 16 * u) * D;
+            ot[u][d] = cat_bf16x8(lds_read_tr16(ol + toff1[d] + rb), lds_read_tr16(ol + toff2[d] + rb));
+            qt[u][d] = cat_bf16x8(lds_read_tr16(ql + toff1[d] + rb), lds_read_tr16(ql + toff2[d] + rb));
+          }
+
         f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
 #pragma unroll
         for (int st = 0; st < NS; ++st) {
-          const bf16x8 aq = *(const bf16x8*)(ql + aoff[st] + 32 * ib * D);
-          const bf16x8 ad = *(const bf16x8*)(ol + aoff[st] + 32 * ib * D);
-          sacc = mfma32(aq, kf[st], sacc);
-          dpacc = mfma32(ad, vf[st], dpacc);
+          sacc = mfma32(aq[st], kf[st], sacc);
+          dpacc = mfma32(ad[st], vf[st], dpacc);
         }
         // sacc[r] = S[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][key kj]
-        const int mbase = i0 + 32 * ib + 4 * hh - kj;
+        unsigned pw[8];
+        auto probs = [&](auto maskc) {
+          constexpr bool MASK = decltype(maskc)::value;
+          const int mbase = i0 + 32 * ib + 4 * hh - kj;
 #pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          const f32x4 l4 = *(const f32x4*)(&lse2_lds[buf][32 * ib + 8 * rg + 4 * hh]);
-          const f32x4 d4 = *(const f32x4*)(&dl_lds[buf][32 * ib + 8 * rg + 4 * hh]);
-          float pr[4], dsr[4];
+          for (int rg = 0; rg < 4; ++rg) {
+            float pr[4], dsr[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            float pv = exp2_fast(fmaf(sacc[r], p.scale_log2, -l4[e]));
-            if (!interior) {
-              const int off = 8 * rg + e;
-              const bool vis = ((unsigned)(mbase + off) < wlim) && (i0 + 32 * ib + 8 * rg + 4 * hh + e < T);
-              if (!vis) pv = 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rg + e;
+              float pv = exp2_fast(fmaf(sacc[r], p.scale_log2, -l4[rg][e]));
+              if (MASK) {
+                const int off = 8 * rg + e;
+                const bool vis = ((unsigned)(mbase + off) < wlim) && (i0 + 32 * ib + 8 * rg + 4 * hh + e < T);
+                pv = vis ? pv : 0.f;
+              }
+              pr[e] = pv;
+              dsr[e] = pv * (dpacc[r] - d4[rg][e]);
             }
-            pr[e] = pv;
-            dsr[e] = pv * (dpacc[r] - d4[e]);
+            pw[2 * rg] = pk_bf16(pr[0], pr[1]);
+            pw[2 * rg + 1] = pk_bf16(pr[2], pr[3]);
+            sw[2 * rg] = pk_bf16(dsr[0], dsr[1]);
+            sw[2 * rg + 1] = pk_bf16(dsr[2], dsr[3]);
           }
-          pw[2 * rg] = pk_bf16(pr[0], pr[1]);
-          pw[2 * rg + 1] = pk_bf16(pr[2], pr[3]);
-          sw[2 * rg] = pk_bf16(dsr[0], dsr[1]);
-          sw[2 * rg + 1] = pk_bf16(dsr[2], dsr[3]);
-        }
+        };
+        if (interior)
+          probs(std::integral_constant<bool, false>{});
+        else
+          probs(std::integral_constant<bool, true>{});
         // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -339,15 +373,10 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
           const u32x4 sq = {sw[4 * u], sw[4 * u + 1], sw[4 * u + 2], sw[4 * u + 3]};
           const bf16x8 pb = __builtin_bit_cast(bf16x8, pq);
           const bf16x8 sb = __builtin_bit_cast(bf16x8, sq);
-          const int rb = (32 * ib + 16 * u) * D;
 #pragma unroll
           for (int d = 0; d < ND; ++d) {
-            const s16x4 o1 = lds_read_tr16(ol + toff1[d] + rb);
-            const s16x4 o2 = lds_read_tr16(ol + toff2[d] + rb);
-            const s16x4 q1 = lds_read_tr16(ql + toff1[d] + rb);
-            const s16x4 q2 = lds_read_tr16(ql + toff2[d] + rb);
-            dv[d] = mfma32(cat_bf16x8(o1, o2), pb, dv[d]);
-            dk[d] = mfma32(cat_bf16x8(q1, q2), sb, dk[d]);
+            dv[d] = mfma32(ot[u][d], pb, dv[d]);
+            dk[d] = mfma32(qt[u][d], sb, dk[d]);
           }
         }
       } else {
@@ -358,7 +387,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) *(u32x2*)(ds_lds + woff[ib][rg]) = (u32x2){sw[2 * rg], sw[2 * rg + 1]};
     }
-    __syncthreads();
+    lds_barrier();
 
     // dQ[i][d] = sum over the 128 keys of dS[i][j] K[j][d] for this wave's
     // d slice; added to the float32 accumulator rows i0 .. i0+63 of head h.
@@ -395,11 +424,14 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_bf16_kernel(BwdParams
         }
       }
     }
+    at_prev2 = at_prev1;
+    at_prev1 = pending;
   };
 
-  for (int step = 0; step < n_steps; step += 2) {
+  for (int step = 0; step < n_steps; step += NBUF) {
     step_fn(step, std::integral_constant<int, 0>{});
     if (step + 1 < n_steps) step_fn(step + 1, std::integral_constant<int, 1>{});
+    if (step + 2 < n_steps) step_fn(step + 2, std::integral_constant<int, 2>{});
   }
 
   // dK (scaled) and dV for this lane's key.

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * T * kvrs + (size_t)g * D;
   // this (b, g)'s rows 0 .. T-1 span (T - 1) * kvrs + D elements
   const unsigned span = (unsigned)(((size_t)(T - 1) * kvrs + D) * 2);
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(kp, span), vrs = make_rsrc(vp, span);
+  const BufDesc krs = buf_desc(kp, span), vrs = buf_desc(vp, span);
 
   // Q as the B operand of S^T = K Q^T: lane (li, hh) holds q[qi][16 s + 8 hh + e].
   bf16x8 qf[NS];
@@ -115,18 +115,16 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
       const unsigned so = (unsigned)j0 * kvrs * 2u;
 #pragma unroll
       for (int n = 0; n < IPW; ++n) {
-        void* dk = &kv_lds[buf][0][(wave * IPW + n) * RPI * D];
-        void* dv = &kv_lds[buf][1][(wave * IPW + n) * RPI * D];
-        buf2lds16(krs, ld_off[n], so, dk);
-        buf2lds16(vrs, ld_off[n], so, dv);
+        dma16(krs, ld_off[n], so, lds_u32(&kv_lds[buf][0][(wave * IPW + n) * RPI * D]));
+        dma16(vrs, ld_off[n], so, lds_u32(&kv_lds[buf][1][(wave * IPW + n) * RPI * D]));
       }
     } else {
 #pragma unroll
       for (int n = 0; n < IPW; ++n) {
         const int j = min(j0 + ld_row[n], T - 1);
         const unsigned vo = (unsigned)(j * kvrs + ld_ch[n] * 8) * 2u;
-        buf2lds16(krs, vo, 0u, &kv_lds[buf][0][(wave * IPW + n) * RPI * D]);
-        buf2lds16(vrs, vo, 0u, &kv_lds[buf][1][(wave * IPW + n) * RPI * D]);
+        dma16(krs, vo, 0u, lds_u32(&kv_lds[buf][0][(wave * IPW + n) * RPI * D]));
+        dma16(vrs, vo, 0u, lds_u32(&kv_lds[buf][1][(wave * IPW + n) * RPI * D]));
       }
     }
   };
@@ -153,8 +151,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
 
   auto tile = [&](int jt, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    wait_vmem();
-    __syncthreads();  // tile jt is in buf; every wave is done with the other buffer
+    wait_vmem();      // this wave's copies of tile jt (the only loads in flight)
+    lds_barrier();    // everyone's copies of tile jt landed; the other buffer is free
     if (jt < t_end) issue_tile(jt + 1, buf ^ 1);
     const unsigned short* kl = kv_lds[buf][0];
     const unsigned short* vl = kv_lds[buf][1];

@@ -65,23 +65,51 @@ __device__ __forceinline__ unsigned pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's 16 bytes land at lds_base + 16 * l, lds_base being wave-uniform.
-__device__ __forceinline__ void g2lds16(const void* gsrc, void* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gsrc,
-                                   (void __attribute__((address_space(3)))*)((size_t)lds_base), 16, 0, 0);
-}
-// Raw buffer resource over [base, base + bytes) (no swizzle, no stride).
+// Raw buffer resource over [base, base + bytes) (no swizzle, no stride), for
+// the buffer atomics.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-// Direct buffer -> LDS copy of 16 bytes per lane: lane l's bytes at
-// base + voffset + soffset land at lds_base + 16 * l (lds_base wave-uniform).
-__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, unsigned voffset, unsigned soffset,
-                                          void* lds_base) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)((size_t)lds_base), 16,
-                                           voffset, soffset, 0, 0);
+// The same descriptor as four dwords (base address, stride 0, num_records,
+// raw dword format), for the inline-assembly loads below.
+typedef u32x4 BufDesc;
+__device__ __forceinline__ BufDesc buf_desc(const void* base, unsigned bytes) {
+  const unsigned long long a = (unsigned long long)(size_t)base;
+  return (BufDesc){(unsigned)a, (unsigned)(a >> 32) & 0xffffu, bytes, 0x00020000u};
 }
+// LDS byte address of a pointer into __shared__ memory, wave-uniform.
+__device__ __forceinline__ unsigned lds_u32(const void* p) {
+  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)p);
+}
+// Direct buffer -> LDS copies: lane l's 16 (dma16) or 4 (dma4) bytes at
+// base + voffset + soffset land at lds + 16 l (4 l); lds is wave-uniform.
+// They are written as inline assembly on purpose: the compiler then leaves
+// them out of its bookkeeping of outstanding vector memory operations and
+// inserts no waits for them (for the builtin it waits for every such copy
+// in flight before any LDS read it cannot prove disjoint, which serialises
+// a prefetch pipeline). Every reader of the destination must therefore wait
+// for the copies itself (wait_vmcnt / wait_vmem_upto, which count them) and
+// then synchronise the workgroup with lds_barrier().
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is reserved; nothing else here relies on its value
+__device__ __forceinline__ void dma16(BufDesc d, unsigned voffset, unsigned soffset, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(d), "s"(soffset)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(BufDesc d, unsigned voffset, unsigned soffset, unsigned lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds), "v"(voffset), "s"(d), "s"(soffset)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+// Workgroup barrier for LDS hand-offs: waits for this wave's own LDS
+// operations, then s_barrier. It is a compiler memory barrier, but unlike
+// __syncthreads it does not wait for outstanding vector memory operations
+// (loads in flight, atomics), which is what lets prefetches overlap compute.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 // sum of the two bf16 halves of w, plus c (v_dot2_f32_bf16 against (1, 1))
 __device__ __forceinline__ float add2_bf16(unsigned w, float c) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -91,6 +119,34 @@ __device__ __forceinline__ float add2_bf16(unsigned w, float c) {
 
 // Wait until all of this wave's global loads (including direct-to-LDS ones) completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+// s_waitcnt with vmcnt = N (0..63) and no wait on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0f70);
+}
+// Wait until at most n (wave-uniform, clamped to 0..63) of this wave's vector
+// memory operations are outstanding.
+__device__ __forceinline__ void wait_vmem_upto(int n) {
+#define NC_VMC_CASE(k) \
+  case k:              \
+    wait_vmcnt<k>();   \
+    break;
+  switch (n < 0 ? 0 : (n > 63 ? 63 : n)) {
+    NC_VMC_CASE(0) NC_VMC_CASE(1) NC_VMC_CASE(2) NC_VMC_CASE(3) NC_VMC_CASE(4) NC_VMC_CASE(5) NC_VMC_CASE(6)
+    NC_VMC_CASE(7) NC_VMC_CASE(8) NC_VMC_CASE(9) NC_VMC_CASE(10) NC_VMC_CASE(11) NC_VMC_CASE(12)
+    NC_VMC_CASE(13) NC_VMC_CASE(14) NC_VMC_CASE(15) NC_VMC_CASE(16) NC_VMC_CASE(17) NC_VMC_CASE(18)
+    NC_VMC_CASE(19) NC_VMC_CASE(20) NC_VMC_CASE(21) NC_VMC_CASE(22) NC_VMC_CASE(23) NC_VMC_CASE(24)
+    NC_VMC_CASE(25) NC_VMC_CASE(26) NC_VMC_CASE(27) NC_VMC_CASE(28) NC_VMC_CASE(29) NC_VMC_CASE(30)
+    NC_VMC_CASE(31) NC_VMC_CASE(32) NC_VMC_CASE(33) NC_VMC_CASE(34) NC_VMC_CASE(35) NC_VMC_CASE(36)
+    NC_VMC_CASE(37) NC_VMC_CASE(38) NC_VMC_CASE(39) NC_VMC_CASE(40) NC_VMC_CASE(41) NC_VMC_CASE(42)
+    NC_VMC_CASE(43) NC_VMC_CASE(44) NC_VMC_CASE(45) NC_VMC_CASE(46) NC_VMC_CASE(47) NC_VMC_CASE(48)
+    NC_VMC_CASE(49) NC_VMC_CASE(50) NC_VMC_CASE(51) NC_VMC_CASE(52) NC_VMC_CASE(53) NC_VMC_CASE(54)
+    NC_VMC_CASE(55) NC_VMC_CASE(56) NC_VMC_CASE(57) NC_VMC_CASE(58) NC_VMC_CASE(59) NC_VMC_CASE(60)
+    NC_VMC_CASE(61) NC_VMC_CASE(62) default: wait_vmcnt<63>(); break;
+  }
+#undef NC_VMC_CASE
+}
 // Wait until at most n (rounded down to 0, 16 or 32; n wave-uniform) of this
 // wave's vector memory operations are outstanding.
 __device__ __forceinline__ void wait_vmem_leq(int n) {
