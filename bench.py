@@ -79,6 +79,9 @@ class Timer:
         self.pairs.setdefault(label, []).append((b, e))
         return b, e
 
+    def add(self, label, b, e):
+        self.pairs.setdefault(label, []).append((b, e))
+
     def totals(self):
         return {k: (sum(b.elapsed_time(e) for b, e in v), len(v)) for k, v in self.pairs.items()}
 
@@ -141,10 +144,12 @@ def main():
         for l in reversed(range(L)):
             b, e = ev("attn_bwd")
             if tm:
-                mb, me = tm.pair("attn_bwd_main")
-                mb.record()  # materialise the events before handing them to the library
-                me.record()
-                native.nc_profile_bwd_main(mb, me)
+                e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                for x in (e0, e1, e2):
+                    x.record()  # materialise the events before handing them to the library
+                tm.add("attn_bwd_dkdv", e0, e1)
+                tm.add("attn_bwd_dq", e1, e2)
+                native.nc_profile_bwd_main(e0, e1, e2)
             b and b.record()
             native.nc_attn_bwd(qp[l], kp[l], vv[l], out[l], lse[l], do[l], wl.windows[l], scale,
                                dq=dqp, dk=dkp, dv=dv, workspace=ws)
@@ -179,16 +184,19 @@ def main():
     flops_f = attn_flops(B, T, H, D, wl.windows, "fwd")
     flops_b = attn_flops(B, T, H, D, wl.windows, "bwd")
     value = (flops_f + flops_b) / (ms_step * 1e-3) / 1e12
+    # flops each kernel performs per step: the forward 4*D per visible pair;
+    # the whole backward is counted as 8*D per pair (dV, dK, dQ and the dP
+    # product); its dK/dV kernel executes 8*D (S, dP, dV, dK) and its dQ
+    # kernel 6*D (S and dP again, then dQ)
+    kflops = {"attn_fwd": flops_f, "attn_bwd": flops_b, "attn_bwd_dkdv": flops_b,
+              "attn_bwd_dq": attn_flops(B, T, H, D, wl.windows, "fwd") * 3 // 2}
     kern = {}
     for label, (ms, n) in tot.items():
         per_step = ms / args.steps
         row = {"ms_per_step": round(per_step, 4), "launches_per_step": n // args.steps,
                "avg_ms_per_launch": round(ms / n, 5)}
-        if label in ("attn_fwd",):
-            row["tflops"] = round(flops_f / (per_step * 1e-3) / 1e12, 2)
-            row["frac_bf16_peak"] = round(row["tflops"] / PEAK_BF16_TFLOPS, 4)
-        if label in ("attn_bwd", "attn_bwd_main"):
-            row["tflops"] = round(flops_b / (per_step * 1e-3) / 1e12, 2)
+        if label in kflops:
+            row["tflops"] = round(kflops[label] / (per_step * 1e-3) / 1e12, 2)
             row["frac_bf16_peak"] = round(row["tflops"] / PEAK_BF16_TFLOPS, 4)
         if label.startswith("prologue"):
             nbytes = 2 * L * (B * T * (H + Hkv) * D * 2) * (1 if label.endswith("fwd") else 1.5)
@@ -236,8 +244,8 @@ def main():
         del kc, vc
 
     # ------------------------------------------------------------- roofline
-    dom = max(("attn_fwd", "attn_bwd_main"), key=lambda k: kern[k]["ms_per_step"])
-    dom_flops = flops_f if dom == "attn_fwd" else flops_b
+    dom = max(("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"), key=lambda k: kern[k]["ms_per_step"])
+    dom_flops = kflops[dom]
     n_launch = kern[dom]["launches_per_step"]
     achieved = dom_flops / n_launch / (kern[dom]["avg_ms_per_launch"] * 1e-3) / 1e12
     tr = measured_traffic(dom)
@@ -245,8 +253,9 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": tr["bytes"] if tr else None,
                 "traffic_split": tr,
-                "note": "achieved = band-counted flops per launch (8*D or 4*D per visible pair, "
-                        "B*H*pairs(T,w) pairs) / average launch time, averaged over the 20 layers"}
+                "note": "achieved = band-counted flops per launch (per visible pair: 4*D fwd, "
+                        "8*D dK/dV kernel, 6*D dQ kernel; B*H*pairs(T,w) pairs) / average launch "
+                        "time, averaged over the 20 layers"}
 
     # --------------------------------------------------------- cpu baseline
     cpu = None

@@ -97,11 +97,10 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
  *   dv_j = sum_{h in group} sum_i P_ij dout_i.
  * dk/dv are summed over the query heads of each group. dq/dk/dv are fully
  * overwritten. q, k, v, out, lse must be those of nc_attn_fwd with the same
- * window and scale. The float32 workspace holds delta [B,H,T], lse*log2(e)
- * [B,H,T] and (bf16) a dq accumulator [B,T,H,D]; its size is
- * nc_attn_bwd_workspace_bytes().
- * dq accumulation uses float32 atomics, so dq can differ in the last bits
- * between runs; dk and dv are deterministic.
+ * window and scale. The float32 workspace holds delta [B,H,T] and
+ * lse*log2(e) [B,H,T]; its size is nc_attn_bwd_workspace_bytes().
+ * dq, dk and dv are deterministic (no atomics; dq comes from its own
+ * query-stationary pass).
  */
 size_t nc_attn_bwd_workspace_bytes(nc_dtype dt, int B, int T, int H, int Hkv, int D);
 nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
@@ -113,13 +112,14 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
 
 /*
  * Measurement aid. While set on the calling thread, every nc_attn_bwd call
- * records begin_event on its stream just before its main kernel (the one
- * that forms dK, dV and the dQ contributions) and end_event just after it,
- * so a caller can time that kernel alone with hipEventElapsedTime. Both are
- * hipEvent_t created by the caller; passing NULL for both clears the
- * setting. Returns NC_ERR_INVALID_ARG if exactly one of them is NULL.
+ * records, on its stream, dkdv_begin just before the kernel that forms dK
+ * and dV, dq_begin between it and the kernel that forms dQ, and end just
+ * after that one, so a caller can time each kernel alone with
+ * hipEventElapsedTime. All are hipEvent_t created by the caller; passing
+ * NULL for all three clears the setting. Returns NC_ERR_INVALID_ARG unless
+ * all three or none are NULL.
  */
-nc_status nc_profile_bwd_main(void* begin_event, void* end_event);
+nc_status nc_profile_bwd_main(void* dkdv_begin, void* dq_begin, void* end);
 
 /*
  * Single-token decode against one layer's KV cache ("nanochat Admin &

@@ -94,7 +94,7 @@ def test_valid_call_without_gpu_reports_device(L):
 def test_bwd_workspace_query_is_pure(L):
     B, T, H, Hkv, D = 2, 100, 4, 2, 64
     stats = -(-(B * H * T * 4) // 256) * 256
-    assert L.nc_attn_bwd_workspace_bytes(BF16, B, T, H, Hkv, D) == 2 * stats + B * T * H * D * 4
+    assert L.nc_attn_bwd_workspace_bytes(BF16, B, T, H, Hkv, D) == 2 * stats
     assert L.nc_attn_bwd_workspace_bytes(F32, B, T, H, Hkv, D) == 2 * stats
     assert L.nc_attn_bwd_workspace_bytes(BF16, B, T, 3, 2, D) == 0
     assert L.nc_attn_bwd_workspace_bytes(BF16, B, T, H, Hkv, 40) == 0
@@ -164,8 +164,9 @@ def test_prologue_validation(L):
 
 
 def test_profile_hook_validation(L):
-    assert L.nc_profile_bwd_main(A, None) == INVALID
-    assert L.nc_profile_bwd_main(None, None) == OK
+    assert L.nc_profile_bwd_main(A, None, None) == INVALID
+    assert L.nc_profile_bwd_main(A, A, None) == INVALID
+    assert L.nc_profile_bwd_main(None, None, None) == OK
 
 
 def test_error_message_is_per_thread(L):

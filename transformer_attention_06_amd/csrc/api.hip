@@ -21,7 +21,7 @@ bool decode_group_supported(int G);
 namespace {
 
 thread_local char g_msg[512] = "";
-thread_local hipEvent_t g_bwd_ev[2] = {nullptr, nullptr};
+thread_local nc::BwdEvents g_bwd_ev = {nullptr, nullptr, nullptr};
 
 nc_status fail(nc_status s, const char* fmt, ...) {
   va_list ap;
@@ -152,8 +152,7 @@ size_t nc_attn_bwd_workspace_bytes(nc_dtype dt, int B, int T, int H, int Hkv, in
   if (check_shape(dt, B, T, H, Hkv, D) != NC_OK) return 0;
   size_t row_stats = (size_t)B * H * T * 4;  // delta, then lse * log2(e)
   row_stats = (row_stats + 255) & ~(size_t)255;
-  const size_t acc = dt == NC_BF16 ? (size_t)B * T * H * D * 4 : 0;
-  return 2 * row_stats + acc;
+  return 2 * row_stats;
 }
 
 nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
@@ -178,19 +177,16 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
   const size_t stat_bytes = ((size_t)B * H * T * 4 + 255) & ~(size_t)255;
   nc::BwdParams p{q, k, v, out, lse, dout, dq, dk, dv, (float*)workspace,
                   (float*)((char*)workspace + stat_bytes),
-                  dt == NC_BF16 ? (float*)((char*)workspace + 2 * stat_bytes) : nullptr,
                   B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f};
   hipStream_t s = (hipStream_t)stream;
-  return finish(dt == NC_BF16 ? nc::launch_attn_bwd_bf16(p, s, g_bwd_ev[0], g_bwd_ev[1])
-                                : nc::launch_attn_bwd_f32(p, s, g_bwd_ev[0], g_bwd_ev[1]),
+  return finish(dt == NC_BF16 ? nc::launch_attn_bwd_bf16(p, s, g_bwd_ev) : nc::launch_attn_bwd_f32(p, s, g_bwd_ev),
                 s, "nc_attn_bwd");
 }
 
-nc_status nc_profile_bwd_main(void* begin_event, void* end_event) {
-  if ((begin_event == nullptr) != (end_event == nullptr))
-    return fail(NC_ERR_INVALID_ARG, "begin_event and end_event must both be set or both be NULL");
-  g_bwd_ev[0] = (hipEvent_t)begin_event;
-  g_bwd_ev[1] = (hipEvent_t)end_event;
+nc_status nc_profile_bwd_main(void* dkdv_begin, void* dq_begin, void* end) {
+  const int set = (dkdv_begin != nullptr) + (dq_begin != nullptr) + (end != nullptr);
+  if (set != 0 && set != 3) return fail(NC_ERR_INVALID_ARG, "the three events must all be set or all be NULL");
+  g_bwd_ev = {(hipEvent_t)dkdv_begin, (hipEvent_t)dq_begin, (hipEvent_t)end};
   g_msg[0] = 0;
   return NC_OK;
 }

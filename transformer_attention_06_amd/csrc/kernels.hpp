@@ -31,7 +31,6 @@ struct BwdParams {
   void* dv;
   float* delta;   // [B, H, T] workspace
   float* lse2;    // [B, H, T] workspace: lse * log2(e)
-  float* dq_acc;  // [B, T, H, D] workspace
   int B, T, H, Hkv, D;
   int window;
   float scale;
@@ -75,9 +74,13 @@ constexpr int decode_chunk(int D, int G) { return (64 / (D / 8)) * decode_keys_p
 
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const FwdParams& p, hipStream_t s);
-// ev_begin / ev_end (may be null) are recorded around the main kernel(s).
-hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end);
-hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s, hipEvent_t ev_begin, hipEvent_t ev_end);
+// Optional events (null = not recorded): before the dK/dV kernel, between
+// it and the dQ kernel, and after the dQ kernel.
+struct BwdEvents {
+  hipEvent_t dkdv_begin, dq_begin, end;
+};
+hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s, const BwdEvents& ev);
+hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s, const BwdEvents& ev);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t s);
 hipError_t launch_rope_table(int T_rope, int D, double base, float* c, float* sn, hipStream_t s);
 hipError_t launch_prologue(const PrologueParams& p, bool bf16, bool backward, hipStream_t s);

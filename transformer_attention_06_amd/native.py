@@ -46,7 +46,7 @@ _SIGS = {
     "nc_attn_fwd": ([_i] * 6 + [_p, _p, _p, _i, _f, _p, _p, _p], _i),
     "nc_attn_bwd_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_bwd": ([_i] * 6 + [_p] * 6 + [_i, _f] + [_p] * 3 + [_p, _sz, _p], _i),
-    "nc_profile_bwd_main": ([_p, _p], _i),
+    "nc_profile_bwd_main": ([_p, _p, _p], _i),
     "nc_attn_decode_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_decode": ([_i] * 6 + [_p] * 4 + [_i, _f, _p, _p, _p, _sz, _p], _i),
     "nc_rope_table": ([_i, _i, _d, _p, _p, _p], _i),
@@ -149,13 +149,13 @@ def nc_attn_bwd(q, k, v, out, lse, dout, window, scale, dq=None, dk=None, dv=Non
     return dq, dk, dv
 
 
-def nc_profile_bwd_main(begin_event=None, end_event=None):
-    """Record two torch.cuda.Event objects (already recorded once, so that
-    they exist) around the main kernel of later nc_attn_bwd calls on this
-    thread; call with no arguments to stop."""
-    b = begin_event.cuda_event if begin_event is not None else None
-    e = end_event.cuda_event if end_event is not None else None
-    _raise_on("nc_profile_bwd_main", lib().nc_profile_bwd_main(b, e))
+def nc_profile_bwd_main(dkdv_begin=None, dq_begin=None, end=None):
+    """Record three torch.cuda.Event objects (already recorded once, so that
+    they exist) before the dK/dV kernel, between it and the dQ kernel, and
+    after the dQ kernel of later nc_attn_bwd calls on this thread; call with
+    no arguments to stop."""
+    evs = [e.cuda_event if e is not None else None for e in (dkdv_begin, dq_begin, end)]
+    _raise_on("nc_profile_bwd_main", lib().nc_profile_bwd_main(*evs))
 
 
 def nc_attn_decode_workspace_bytes(dtype_code, B, H, Hkv, D, T_max):
