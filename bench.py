@@ -147,8 +147,8 @@ def main():
                 e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                 for x in (e0, e1, e2):
                     x.record()  # materialise the events before handing them to the library
-                tm.add("attn_bwd_dkdv", e0, e1)
-                tm.add("attn_bwd_dq", e1, e2)
+                tm.add("attn_bwd_dq", e0, e1)
+                tm.add("attn_bwd_dkdv", e1, e2)
                 native.nc_profile_bwd_main(e0, e1, e2)
             b and b.record()
             native.nc_attn_bwd(qp[l], kp[l], vv[l], out[l], lse[l], do[l], wl.windows[l], scale,

@@ -112,14 +112,14 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
 
 /*
  * Measurement aid. While set on the calling thread, every nc_attn_bwd call
- * records, on its stream, dkdv_begin just before the kernel that forms dK
- * and dV, dq_begin between it and the kernel that forms dQ, and end just
- * after that one, so a caller can time each kernel alone with
- * hipEventElapsedTime. All are hipEvent_t created by the caller; passing
- * NULL for all three clears the setting. Returns NC_ERR_INVALID_ARG unless
- * all three or none are NULL.
+ * records, on its stream, dq_begin just before the kernel that forms dQ
+ * (for bf16 it also forms the row statistics), dkdv_begin between it and
+ * the kernel that forms dK and dV, and end just after that one, so a caller
+ * can time each kernel alone with hipEventElapsedTime. All are hipEvent_t
+ * created by the caller; passing NULL for all three clears the setting.
+ * Returns NC_ERR_INVALID_ARG unless all three or none are NULL.
  */
-nc_status nc_profile_bwd_main(void* dkdv_begin, void* dq_begin, void* end);
+nc_status nc_profile_bwd_main(void* dq_begin, void* dkdv_begin, void* end);
 
 /*
  * Single-token decode against one layer's KV cache ("nanochat Admin &

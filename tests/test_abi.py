@@ -164,7 +164,7 @@ def test_prologue_validation(L):
 
 
 def test_profile_hook_validation(L):
-    assert L.nc_profile_bwd_main(A, None, None) == INVALID
+    assert L.nc_profile_bwd_main(A, None, None) == INVALID  # dq_begin, dkdv_begin, end
     assert L.nc_profile_bwd_main(A, A, None) == INVALID
     assert L.nc_profile_bwd_main(None, None, None) == OK
 

@@ -183,10 +183,10 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
                 s, "nc_attn_bwd");
 }
 
-nc_status nc_profile_bwd_main(void* dkdv_begin, void* dq_begin, void* end) {
-  const int set = (dkdv_begin != nullptr) + (dq_begin != nullptr) + (end != nullptr);
+nc_status nc_profile_bwd_main(void* dq_begin, void* dkdv_begin, void* end) {
+  const int set = (dq_begin != nullptr) + (dkdv_begin != nullptr) + (end != nullptr);
   if (set != 0 && set != 3) return fail(NC_ERR_INVALID_ARG, "the three events must all be set or all be NULL");
-  g_bwd_ev = {(hipEvent_t)dkdv_begin, (hipEvent_t)dq_begin, (hipEvent_t)end};
+  g_bwd_ev = {(hipEvent_t)dq_begin, (hipEvent_t)dkdv_begin, (hipEvent_t)end};
   g_msg[0] = 0;
   return NC_OK;
 }

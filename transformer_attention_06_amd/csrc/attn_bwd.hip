@@ -12,8 +12,16 @@
 // and "NanoChat.NET" catalog pages, "Model & kernels"; the formulas are the
 // plain chain rule through the softmax.)
 //
-// bf16 path, three kernels, no atomics:
-//   pre:  delta_i = <dout_i, out_i> and lse_i * log2(e) in float32.
+// bf16 path, two kernels, no atomics:
+//   dq:   one workgroup per (b, h, 128-query tile), the forward kernel's
+//         structure: q and dO stay in registers as B operands, K/V tiles of
+//         64 keys stream through double-buffered LDS, S^T = K Q^T and
+//         dP^T = V dO^T give one query column per lane, dS is formed from
+//         the row statistics, and dQ^T += K^T dS^T takes K^T from LDS
+//         transpose reads. S and dP are recomputed here rather than
+//         exchanged with dkdv, which keeps dQ free of float atomics. It
+//         forms the row statistics delta_i = <dout_i, out_i> and
+//         lse_i * log2(e) itself and stores them for dkdv.
 //   dkdv: one workgroup per (b, kv head, 128-key tile); each of the 4 waves
 //         keeps 32 keys' K and V fragments in registers and accumulates dK^T
 //         and dV^T for them over every query head of the GQA group and every
@@ -23,14 +31,8 @@
 //         Q^T are LDS transpose reads. Q/dO tiles and the per-row
 //         statistics stream into LDS with buffer-to-LDS loads running
 //         NBUF - 1 steps ahead; LDS addresses are per-lane constants.
-//   dq:   one workgroup per (b, h, 128-query tile), the forward kernel's
-//         structure: q and dO stay in registers as B operands, K/V tiles of
-//         64 keys stream through double-buffered LDS, S^T = K Q^T and
-//         dP^T = V dO^T give one query column per lane, dS is formed from
-//         the saved statistics, and dQ^T += K^T dS^T takes K^T from LDS
-//         transpose reads. S and dP are recomputed here rather than
-//         exchanged with dkdv, which keeps dQ free of float atomics.
-// f32 path: plain per-key (dk, dv) and per-query (dq) loops in float32.
+// f32 path: row statistics, then plain per-query (dq) and per-key (dk, dv)
+// loops in float32.
 
 #include <math.h>
 
@@ -50,9 +52,9 @@ constexpr int DQ_BM = 128;  // queries per dq workgroup (32 per wave)
 constexpr int DQ_BN = 64;   // keys per dq tile
 
 // --------------------------------------------------------------------------
-// delta = rowsum(dout * out), lse2 = lse * log2(e) (float32).
-template <int D, bool BF16>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+// float32 path: delta = rowsum(dout * out), lse2 = lse * log2(e).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_pre_f32_kernel(BwdParams p) {
   constexpr int LPR = D / 8;  // lanes per row, 8 elements each
   const long rows = (long)p.B * p.T * p.H;
   const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -61,23 +63,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   float acc = 0.f;
   if (row < rows) {
     const size_t off = (size_t)row * D + c * 8;
-    float a[8], o[8];
-    if (BF16) {
-      unpack8_bf16(*(const u32x4*)((const unsigned short*)p.dout + off), a);
-      unpack8_bf16(*(const u32x4*)((const unsigned short*)p.out + off), o);
-    } else {
-      const f32x4* pa = (const f32x4*)((const float*)p.dout + off);
-      const f32x4* po = (const f32x4*)((const float*)p.out + off);
-      const f32x4 a0 = pa[0], a1 = pa[1], o0 = po[0], o1 = po[1];
-      for (int i = 0; i < 4; ++i) {
-        a[i] = a0[i];
-        a[4 + i] = a1[i];
-        o[i] = o0[i];
-        o[4 + i] = o1[i];
-      }
-    }
+    const f32x4* pa = (const f32x4*)((const float*)p.dout + off);
+    const f32x4* po = (const f32x4*)((const float*)p.out + off);
+    const f32x4 a0 = pa[0], a1 = pa[1], o0 = po[0], o1 = po[1];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf(a[i], o[i], acc);
+    for (int i = 0; i < 4; ++i) acc = fmaf(a1[i], o1[i], fmaf(a0[i], o0[i], acc));
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += shfl_xor(acc, m);
@@ -393,9 +383,28 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void attn_bwd_dq_kernel(BwdParams p
     qf[s] = __builtin_bit_cast(bf16x8, a);
     of[s] = __builtin_bit_cast(bf16x8, c);
   }
+  // This lane's row statistics, formed here and also stored for the dK/dV
+  // kernel that runs next: delta = <dout, out> (the two half-waves hold the
+  // two halves of d) and lse * log2(e).
   const size_t si = ((size_t)b * p.H + h) * T + (q_valid ? qi : 0);
-  const float l2 = q_valid ? p.lse2[si] : 0.f;
-  const float dl = q_valid ? p.delta[si] : 0.f;
+  float dl = 0.f;
+  if (q_valid) {
+    const unsigned short* opr = (const unsigned short*)p.out + ((size_t)b * T + qi) * qrs + (size_t)h * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float o8[8], d8[8];
+      unpack8_bf16(*(const u32x4*)(opr + 16 * s + 8 * hh), o8);
+      unpack8_bf16(__builtin_bit_cast(u32x4, of[s]), d8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dl = fmaf(d8[e], o8[e], dl);
+    }
+  }
+  dl += shfl_xor(dl, 32);
+  const float l2 = q_valid ? p.lse[si] * kLog2e : 0.f;
+  if (q_valid && hh == 0) {
+    p.delta[si] = dl;
+    p.lse2[si] = l2;
+  }
 
   const bool full = p.window <= 0;
   const int win = p.window;
@@ -624,10 +633,10 @@ __global__ __launch_bounds__(64) void bwd_dq_f32_kernel(BwdParams p) {
 }
 
 
-template <int D, bool BF16>
+template <int D>
 hipError_t launch_pre(const BwdParams& p, hipStream_t s) {
   const long threads = (long)p.B * p.T * p.H * (D / 8);
-  bwd_pre_kernel<D, BF16><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(p);
+  bwd_pre_f32_kernel<D><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -635,29 +644,29 @@ hipError_t record(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev,
 
 template <int D>
 hipError_t launch_bf16(const BwdParams& p, hipStream_t s, const BwdEvents& ev) {
-  hipError_t e = launch_pre<D, true>(p, s);
-  if (e != hipSuccess) return e;
-  if ((e = record(ev.dkdv_begin, s)) != hipSuccess) return e;
-  const int nkt = (p.T + BWD_BN - 1) / BWD_BN;
-  attn_bwd_dkdv_kernel<D><<<nkt * p.Hkv * p.B, BWD_THREADS, 0, s>>>(p);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e;
+  // the dQ kernel first: it also forms the row statistics the dK/dV kernel reads
   if ((e = record(ev.dq_begin, s)) != hipSuccess) return e;
   const int nqt = (p.T + DQ_BM - 1) / DQ_BM;
   attn_bwd_dq_kernel<D><<<nqt * p.H * p.B, BWD_THREADS, 0, s>>>(p);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = record(ev.dkdv_begin, s)) != hipSuccess) return e;
+  const int nkt = (p.T + BWD_BN - 1) / BWD_BN;
+  attn_bwd_dkdv_kernel<D><<<nkt * p.Hkv * p.B, BWD_THREADS, 0, s>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record(ev.end, s);
 }
 
 template <int D>
 hipError_t launch_f32(const BwdParams& p, hipStream_t s, const BwdEvents& ev) {
-  hipError_t e = launch_pre<D, false>(p, s);
-  if (e != hipSuccess) return e;
-  if ((e = record(ev.dkdv_begin, s)) != hipSuccess) return e;
-  bwd_dkdv_f32_kernel<D><<<dim3((p.T + 63) / 64, p.Hkv, p.B), 64, 0, s>>>(p);
-  e = hipGetLastError();
+  hipError_t e = launch_pre<D>(p, s);
   if (e != hipSuccess) return e;
   if ((e = record(ev.dq_begin, s)) != hipSuccess) return e;
   bwd_dq_f32_kernel<D><<<dim3((p.T + 63) / 64, p.H, p.B), 64, 0, s>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if ((e = record(ev.dkdv_begin, s)) != hipSuccess) return e;
+  bwd_dkdv_f32_kernel<D><<<dim3((p.T + 63) / 64, p.Hkv, p.B), 64, 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   return record(ev.end, s);

@@ -74,10 +74,10 @@ constexpr int decode_chunk(int D, int G) { return (64 / (D / 8)) * decode_keys_p
 
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const FwdParams& p, hipStream_t s);
-// Optional events (null = not recorded): before the dK/dV kernel, between
-// it and the dQ kernel, and after the dQ kernel.
+// Optional events (null = not recorded): before the dQ kernel, between it
+// and the dK/dV kernel, and after the dK/dV kernel.
 struct BwdEvents {
-  hipEvent_t dkdv_begin, dq_begin, end;
+  hipEvent_t dq_begin, dkdv_begin, end;
 };
 hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s, const BwdEvents& ev);
 hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s, const BwdEvents& ev);

@@ -149,12 +149,12 @@ def nc_attn_bwd(q, k, v, out, lse, dout, window, scale, dq=None, dk=None, dv=Non
     return dq, dk, dv
 
 
-def nc_profile_bwd_main(dkdv_begin=None, dq_begin=None, end=None):
+def nc_profile_bwd_main(dq_begin=None, dkdv_begin=None, end=None):
     """Record three torch.cuda.Event objects (already recorded once, so that
-    they exist) before the dK/dV kernel, between it and the dQ kernel, and
-    after the dQ kernel of later nc_attn_bwd calls on this thread; call with
-    no arguments to stop."""
-    evs = [e.cuda_event if e is not None else None for e in (dkdv_begin, dq_begin, end)]
+    they exist) before the dQ kernel, between it and the dK/dV kernel, and
+    after the dK/dV kernel of later nc_attn_bwd calls on this thread; call
+    with no arguments to stop."""
+    evs = [e.cuda_event if e is not None else None for e in (dq_begin, dkdv_begin, end)]
     _raise_on("nc_profile_bwd_main", lib().nc_profile_bwd_main(*evs))
 
 
