@@ -399,7 +399,7 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void attn_bwd_dq_kernel(BwdParams p
       for (int e = 0; e < 8; ++e) dl = fmaf(d8[e], o8[e], dl);
     }
   }
-  dl += shfl_xor(dl, 32);
+  dl = sum_mod<32>(dl);
   const float l2 = q_valid ? p.lse[si] * kLog2e : 0.f;
   if (q_valid && hh == 0) {
     p.delta[si] = dl;

@@ -179,10 +179,15 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
         for (int r = 0; r < 16; ++r)
           if ((unsigned)(base - (32 * jb + 8 * (r >> 2) + (r & 3))) >= wlim) s[jb][r] = -INFINITY;
     }
-    float mx = fmaxf(fmaxf(s[0][0], s[0][1]), s[1][0]);
+    // tile max of this query: four independent chains, then the two half-waves
+    float m4[4];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s[0][r]), s[1][r]);
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    for (int c = 0; c < 4; ++c) {
+      m4[c] = fmaxf(s[0][c], s[1][c]);
+#pragma unroll
+      for (int r = c + 4; r < 16; r += 4) m4[c] = fmaxf(fmaxf(m4[c], s[0][r]), s[1][r]);
+    }
+    const float mx = max_mod<32>(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
     // The reference max only moves up when the tile max exceeds it by more than
     // 8 (a factor 2^8): the exponentials stay <= 256 and O is rescaled rarely.
     const float mt = mx * p.scale_log2;
@@ -239,7 +244,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
     if (jt + 1 <= t_end) tile(jt + 1, std::integral_constant<int, 1>{});
   }
 
-  const float lt = lsum + shfl_xor(lsum, 32);
+  const float lt = sum_mod<32>(lsum);
   if (q_valid) {
     const float inv = 1.f / lt;
     unsigned short* op = (unsigned short*)p.out + ((size_t)b * T + qi) * qrs + (size_t)h * D;

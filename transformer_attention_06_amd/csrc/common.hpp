@@ -183,6 +183,34 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Reductions over lanes with equal l % S (S = 4, 8, 16 or 32): every lane
+// gets the sum (or maximum) over its class, with no LDS traffic. Inside a
+// 16-lane row the partners come from DPP row rotations (x[i] + x[i - S] and
+// so on, mod 16); across rows from v_permlane16_swap (rows 0<->1, 2<->3) and
+// v_permlane32_swap (lanes l <-> l ^ 32). Either swap returns the pair of
+// values in some order in its two results, so combining both results is
+// symmetric and needs no lane select.
+__device__ __forceinline__ unsigned f2u(float x) { return __builtin_bit_cast(unsigned, x); }
+__device__ __forceinline__ float u2f(unsigned x) { return __builtin_bit_cast(float, x); }
+template <bool MAX>
+__device__ __forceinline__ float comb(float a, float b) { return MAX ? fmaxf(a, b) : a + b; }
+template <int S, bool MAX>
+__device__ __forceinline__ float reduce_mod(float x) {
+  static_assert(S == 4 || S == 8 || S == 16 || S == 32, "lane class stride");
+  if (S == 4) x = comb<MAX>(x, dpp_mov<0x124>(x));  // row_ror:4
+  if (S <= 8) x = comb<MAX>(x, dpp_mov<0x128>(x));  // row_ror:8
+  if (S <= 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(f2u(x), f2u(x), false, false);
+    x = comb<MAX>(u2f(r[0]), u2f(r[1]));
+  }
+  const auto r = __builtin_amdgcn_permlane32_swap(f2u(x), f2u(x), false, false);
+  return comb<MAX>(u2f(r[0]), u2f(r[1]));
+}
+template <int S>
+__device__ __forceinline__ float sum_mod(float x) { return reduce_mod<S, false>(x); }
+template <int S>
+__device__ __forceinline__ float max_mod(float x) { return reduce_mod<S, true>(x); }
+
 // ---------------------------------------------------------------------------
 // LDS transpose read (ds_read_b64_tr_b16). Within each group of 16 lanes,
 // lane t supplies the address of 4 consecutive 16-bit elements; the result

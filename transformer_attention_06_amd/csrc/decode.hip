@@ -13,8 +13,9 @@
 //   D = 128). All of a group's K and V rows are requested before any is used
 //   (one memory round trip per wave), the dot products are finished with DPP
 //   exchanges inside the group, the softmax is taken in one pass over the
-//   known scores, and the groups are merged with cross-row exchanges. One
-//   partial (acc[D], m, l) per (row, query head, chunk) goes to the workspace.
+//   known scores, and the groups are merged with DPP row rotations and
+//   permlane swaps (no LDS traffic). One partial (acc[D], m, l) per
+//   (row, query head, chunk) goes to the workspace.
 //   Chunks outside a row's key range exit without reading anything.
 // decode_combine: merges a row's partials into out and lse. A length outside
 //   1..T_max yields NaN out and lse for that row.
@@ -133,8 +134,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
       m = fmaxf(m, s[u]);
     }
     // the wave's maximum (at least one position is present), then one pass
-#pragma unroll
-    for (int msk = LPR; msk < 64; msk <<= 1) m = fmaxf(m, shfl_xor(m, msk));
+    m = max_mod<LPR>(m);
     float l = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < KPG; ++u) {
@@ -145,12 +145,9 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = fmaf(pe, vf[e], acc[e]);
     }
+    l = sum_mod<LPR>(l);
 #pragma unroll
-    for (int msk = LPR; msk < 64; msk <<= 1) {
-      l += shfl_xor(l, msk);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += shfl_xor(acc[e], msk);
-    }
+    for (int e = 0; e < 8; ++e) acc[e] = sum_mod<LPR>(acc[e]);
     if (grp == 0) {
       float* dst = p.part + (((size_t)b * H + g * G + hq) * p.n_split + sp) * (D + 2);
 #pragma unroll
