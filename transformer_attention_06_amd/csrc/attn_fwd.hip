@@ -51,12 +51,20 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   // [buffer][K or V][tile]: the next tile streams into one buffer while the other is read
   __shared__ __attribute__((aligned(16))) unsigned short kv_lds[2][2][TILE];
 
+  // Under the full causal mask a workgroup takes query tiles nqt-1-r and r
+  // of one (b, h), in that order: their key counts add up to the same for
+  // every r, so the workgroups are of equal weight and the grid has no tail
+  // of heavy late tiles; the first K/V tile of the second query tile is
+  // loaded while the first one finishes. Under a window the per-tile work
+  // is nearly flat already: one query tile per workgroup, late tiles first.
   const int T = p.T;
   const int nqt = (T + FWD_BM - 1) / FWD_BM;
-  const int N = nqt * p.H * p.B;
+  const bool paired = p.window <= 0;
+  const int nunit = paired ? (nqt + 1) / 2 : nqt;
+  const int N = nunit * p.H * p.B;
   const int logical = xcd_remap(blockIdx.x, N);
-  const int bh = logical / nqt;
-  const int qt = nqt - 1 - (logical - bh * nqt);  // late (heavier) query tiles first
+  const int bh = logical / nunit;
+  const int r_pair = logical - bh * nunit;
   const int b = bh / p.H, h = bh - b * p.H;
   const int g = h / (p.H / p.Hkv);
 
@@ -64,10 +72,6 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hh = lane >> 5;
   const int grp = lane >> 4, t16 = lane & 15;
-  const int q0 = qt * FWD_BM;
-  const int qw = q0 + wave * 32;
-  const int qi = qw + li;
-  const bool q_valid = qi < T;
 
   const size_t qrs = (size_t)p.H * D;
   const unsigned kvrs = (unsigned)(p.Hkv * D);  // elements between consecutive positions
@@ -78,22 +82,16 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   const unsigned span = (unsigned)(((size_t)(T - 1) * kvrs + D) * 2);
   const BufDesc krs = buf_desc(kp, span), vrs = buf_desc(vp, span);
 
-  // Q as the B operand of S^T = K Q^T: lane (li, hh) holds q[qi][16 s + 8 hh + e].
-  bf16x8 qf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (q_valid) w = *(const u32x4*)(qp + (size_t)qi * qrs + 16 * s + 8 * hh);
-    qf[s] = __builtin_bit_cast(bf16x8, w);
-  }
-
   const bool full = p.window <= 0;
   const int win = p.window;
   // key j is visible to query i iff (unsigned)(i - j) < wlim
   const unsigned wlim = full ? 0x80000000u : (unsigned)win;
-  const int kv_hi = min(T - 1, q0 + FWD_BM - 1);
-  const int kv_lo = full ? 0 : max(0, q0 - win + 1);
-  const int t_begin = kv_lo / FWD_BN, t_end = kv_hi / FWD_BN;
+  // key tiles [first, last] of query tile qt
+  auto tile_range = [&](int qt, int& first, int& last) {
+    const int q0 = qt * FWD_BM;
+    first = (full ? 0 : max(0, q0 - win + 1)) / FWD_BN;
+    last = min(T - 1, q0 + FWD_BM - 1) / FWD_BN;
+  };
 
   // Tile loads: lane l of instruction n writes tile row (inst*RPI + l/NC),
   // physical chunk l%NC, which holds logical chunk (l%NC) ^ swz(row). The
@@ -143,17 +141,24 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
     voff2[d] = swz_off<NC>(4 * hh + (t16 >> 2) + 8, col);
   }
 
+  // state of the query tile being processed
+  int qw = 0, qi = 0;    // first query of this wave, this lane's query
+  bool q_valid = false;
+  int t_end = 0;         // its last key tile
+  int next_first = -1;   // first key tile of the next query tile (-1: none)
+  bf16x8 qf[NS];         // q as the B operand of S^T = K Q^T: q[qi][16 s + 8 hh + e]
   float m2 = -INFINITY;  // running reference max (log2 units) for this query
   float lsum = 0.f;      // running sum over this lane's half of the keys
   f32x16 o[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) o[d] = (f32x16){};
 
-  auto tile = [&](int jt, auto bufc) {
+  auto tile = [&](int jt, auto bufc) __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     wait_vmem();      // this wave's copies of tile jt (the only loads in flight)
     lds_barrier();    // everyone's copies of tile jt landed; the other buffer is free
-    if (jt < t_end) issue_tile(jt + 1, buf ^ 1);
+    if (jt < t_end)
+      issue_tile(jt + 1, buf ^ 1);
+    else if (next_first >= 0)
+      issue_tile(next_first, buf ^ 1);
     const unsigned short* kl = kv_lds[buf][0];
     const unsigned short* vl = kv_lds[buf][1];
 
@@ -238,26 +243,59 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
       }
   };
 
-  issue_tile(t_begin, 0);
-  for (int jt = t_begin; jt <= t_end; jt += 2) {
-    tile(jt, std::integral_constant<int, 0>{});
-    if (jt + 1 <= t_end) tile(jt + 1, std::integral_constant<int, 1>{});
-  }
+  auto run = [&](int qt, int t_begin, auto startc) __attribute__((always_inline)) {
+    constexpr int S0 = decltype(startc)::value;  // buffer of the first key tile
+    qw = qt * FWD_BM + wave * 32;
+    qi = qw + li;
+    q_valid = qi < T;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      u32x4 w = {0u, 0u, 0u, 0u};
+      if (q_valid) w = *(const u32x4*)(qp + (size_t)qi * qrs + 16 * s + 8 * hh);
+      qf[s] = __builtin_bit_cast(bf16x8, w);
+    }
+    m2 = -INFINITY;
+    lsum = 0.f;
+#pragma unroll
+    for (int d = 0; d < ND; ++d) o[d] = (f32x16){};
+    for (int jt = t_begin; jt <= t_end; jt += 2) {
+      tile(jt, std::integral_constant<int, S0>{});
+      if (jt + 1 <= t_end) tile(jt + 1, std::integral_constant<int, S0 ^ 1>{});
+    }
 
-  const float lt = sum_mod<32>(lsum);
-  if (q_valid) {
-    const float inv = 1.f / lt;
-    unsigned short* op = (unsigned short*)p.out + ((size_t)b * T + qi) * qrs + (size_t)h * D;
+    const float lt = sum_mod<32>(lsum);
+    if (q_valid) {
+      const float inv = 1.f / lt;
+      unsigned short* op = (unsigned short*)p.out + ((size_t)b * T + qi) * qrs + (size_t)h * D;
 #pragma unroll
-    for (int d = 0; d < ND; ++d)
+      for (int d = 0; d < ND; ++d)
 #pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        u32x2 w;
-        w[0] = pk_bf16(o[d][4 * rg] * inv, o[d][4 * rg + 1] * inv);
-        w[1] = pk_bf16(o[d][4 * rg + 2] * inv, o[d][4 * rg + 3] * inv);
-        *(u32x2*)(op + 32 * d + 8 * rg + 4 * hh) = w;
-      }
-    if (hh == 0) p.lse[((size_t)b * p.H + h) * T + qi] = (m2 + __builtin_log2f(lt)) * kLn2;
+        for (int rg = 0; rg < 4; ++rg) {
+          u32x2 w;
+          w[0] = pk_bf16(o[d][4 * rg] * inv, o[d][4 * rg + 1] * inv);
+          w[1] = pk_bf16(o[d][4 * rg + 2] * inv, o[d][4 * rg + 3] * inv);
+          *(u32x2*)(op + 32 * d + 8 * rg + 4 * hh) = w;
+        }
+      if (hh == 0) p.lse[((size_t)b * p.H + h) * T + qi] = (m2 + __builtin_log2f(lt)) * kLn2;
+    }
+  };
+
+  const int qt_a = nqt - 1 - r_pair, qt_b = r_pair;
+  const int n_pass = paired && qt_b < qt_a ? 2 : 1;
+  int first[2], last[2];
+  tile_range(qt_a, first[0], last[0]);
+  tile_range(qt_b, first[1], last[1]);
+  issue_tile(first[0], 0);
+  int start = 0;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    // (uniform by construction; said so for the scalar operands of the copies)
+    t_end = __builtin_amdgcn_readfirstlane(last[pass]);
+    next_first = __builtin_amdgcn_readfirstlane(pass + 1 < n_pass ? first[pass + 1] : -1);
+    if (start == 0)
+      run(pass == 0 ? qt_a : qt_b, first[pass], std::integral_constant<int, 0>{});
+    else
+      run(pass == 0 ? qt_a : qt_b, first[pass], std::integral_constant<int, 1>{});
+    start = (start + last[pass] - first[pass] + 1) & 1;
   }
 }
 
@@ -308,7 +346,7 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(FwdParams p) {
 
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s) {
   const int nqt = (p.T + FWD_BM - 1) / FWD_BM;
-  const dim3 grid(nqt * p.H * p.B), block(FWD_THREADS);
+  const dim3 grid((p.window <= 0 ? (nqt + 1) / 2 : nqt) * p.H * p.B), block(FWD_THREADS);
   switch (p.D) {
     case 32: attn_fwd_bf16_kernel<32><<<grid, block, 0, s>>>(p); break;
     case 64: attn_fwd_bf16_kernel<64><<<grid, block, 0, s>>>(p); break;
