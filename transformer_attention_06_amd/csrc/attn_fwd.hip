@@ -285,12 +285,16 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   int first[2], last[2];
   tile_range(qt_a, first[0], last[0]);
   tile_range(qt_b, first[1], last[1]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {  // uniform by construction; said so for the copies' scalar operands
+    first[i] = __builtin_amdgcn_readfirstlane(first[i]);
+    last[i] = __builtin_amdgcn_readfirstlane(last[i]);
+  }
   issue_tile(first[0], 0);
   int start = 0;
   for (int pass = 0; pass < n_pass; ++pass) {
-    // (uniform by construction; said so for the scalar operands of the copies)
-    t_end = __builtin_amdgcn_readfirstlane(last[pass]);
-    next_first = __builtin_amdgcn_readfirstlane(pass + 1 < n_pass ? first[pass + 1] : -1);
+    t_end = last[pass];
+    next_first = pass + 1 < n_pass ? first[pass + 1] : -1;
     if (start == 0)
       run(pass == 0 ? qt_a : qt_b, first[pass], std::integral_constant<int, 0>{});
     else
