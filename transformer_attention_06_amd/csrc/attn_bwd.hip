@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(BwdParams p) {
 
 // --------------------------------------------------------------------------
 // dK and dV: one workgroup per (b, kv head, 128-key tile), 4 waves of 32 keys.
-template <int D>
+template <int D, bool PAIRED>
 __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
   constexpr int NC = D / 8;  // chunks per row of the q/dO tiles (swizzled)
   constexpr int NS = D / 16;
@@ -99,12 +99,16 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
   __shared__ __attribute__((aligned(16))) float lse2_lds[NBUF][BWD_BM];
   __shared__ __attribute__((aligned(16))) float dl_lds[NBUF][BWD_BM];
 
+  // Under the full causal mask a workgroup takes key tiles r and nkt-1-r of
+  // one (b, kv head), in that order (their query counts add up to the same
+  // for every r: equal weight, no tail); else one key tile, early first.
   const int T = p.T;
   const int nkt = (T + BWD_BN - 1) / BWD_BN;
-  const int N = nkt * p.Hkv * p.B;
+  const int nunit = PAIRED ? (nkt + 1) / 2 : nkt;
+  const int N = nunit * p.Hkv * p.B;
   const int logical = xcd_remap(blockIdx.x, N);
-  const int bg = logical / nkt;
-  const int kt = logical - bg * nkt;  // early key tiles (most queries) first
+  const int bg = logical / nunit;
+  const int r_pair = logical - bg * nunit;
   const int b = bg / p.Hkv, g = bg - b * p.Hkv;
   const int G = p.H / p.Hkv;
 
@@ -112,43 +116,18 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int li = lane & 31, hh = lane >> 5;
   const int grp = lane >> 4, t16 = lane & 15;
-  const int j0 = kt * BWD_BN;
-  const int kw = j0 + wave * 32;
-  const int kj = kw + li;  // this lane's key
 
   const unsigned qrs = (unsigned)(p.H * D);
   const unsigned kvrs = (unsigned)(p.Hkv * D);
   const unsigned short* kp = (const unsigned short*)p.k + (size_t)b * T * kvrs + (size_t)g * D;
   const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * T * kvrs + (size_t)g * D;
 
-  // K and V fragments of this lane's key: lane (li, hh) holds x[kj][16 s + 8 hh + e].
-  bf16x8 kf[NS], vf[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-    if (kj < T) {
-      a = *(const u32x4*)(kp + (size_t)kj * kvrs + 16 * s + 8 * hh);
-      c = *(const u32x4*)(vp + (size_t)kj * kvrs + 16 * s + 8 * hh);
-    }
-    kf[s] = __builtin_bit_cast(bf16x8, a);
-    vf[s] = __builtin_bit_cast(bf16x8, c);
-  }
   const int tr_row = t16 >> 2;
   const int tr_col = 16 * (grp & 1) + 4 * (t16 & 3);
-
-  f32x16 dk[ND], dv[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    dk[d] = (f32x16){};
-    dv[d] = (f32x16){};
-  }
 
   const bool full = p.window <= 0;
   const int win = p.window;
   const unsigned wlim = full ? 0x80000000u : (unsigned)win;
-  const int i_last = full ? T - 1 : min(T - 1, j0 + BWD_BN - 1 + win - 1);
-  const int it_begin = j0 / BWD_BM, n_it = i_last / BWD_BM - it_begin + 1;
-  const int n_steps = G * n_it;
 
   // ---- per-lane constant LDS offsets ----
   // q/dO operand rows li (+32 ib) at chunk 2 st + hh
@@ -174,158 +153,189 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
     ld_off[n] = (unsigned)(row * qrs + ld_ch[n] * 8) * 2u;
   }
   const unsigned qspan = (unsigned)(((size_t)(T - 1) * qrs + D) * 2);
-  auto issue_step = [&](int step, int buf) {
-    const int hq = step / n_it;
-    const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
-    const int h = g * G + hq;
-    const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
-    const unsigned short* dop = (const unsigned short*)p.dout + (size_t)b * T * qrs + (size_t)h * D;
-    const BufDesc qrsr = buf_desc(qp, qspan), orsr = buf_desc(dop, qspan);
-    if (i0 + BWD_BM <= T) {
-      const unsigned so = (unsigned)i0 * qrs * 2u;
+  auto run = [&](int kt) __attribute__((always_inline)) {
+    const int j0 = kt * BWD_BN;
+    const int kw = j0 + wave * 32;
+    const int kj = kw + li;  // this lane's key
+    const int i_last = full ? T - 1 : min(T - 1, j0 + BWD_BN - 1 + win - 1);
+    const int it_begin = j0 / BWD_BM, n_it = i_last / BWD_BM - it_begin + 1;
+    const int n_steps = G * n_it;
+    // K and V fragments of this lane's key: lane (li, hh) holds x[kj][16 s + 8 hh + e].
+    bf16x8 kf[NS], vf[NS];
+    f32x16 dk[ND], dv[ND];
 #pragma unroll
-      for (int n = 0; n < QIPW; ++n) {
-        dma16(qrsr, ld_off[n], so, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
-        dma16(orsr, ld_off[n], so, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
+    for (int s = 0; s < NS; ++s) {
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (kj < T) {
+        a = *(const u32x4*)(kp + (size_t)kj * kvrs + 16 * s + 8 * hh);
+        c = *(const u32x4*)(vp + (size_t)kj * kvrs + 16 * s + 8 * hh);
       }
-    } else {
-#pragma unroll
-      for (int n = 0; n < QIPW; ++n) {
-        const int i = min(i0 + ld_row[n], T - 1);
-        const unsigned vo = (unsigned)(i * qrs + ld_ch[n] * 8) * 2u;
-        dma16(qrsr, vo, 0u, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
-        dma16(orsr, vo, 0u, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
-      }
+      kf[s] = __builtin_bit_cast(bf16x8, a);
+      vf[s] = __builtin_bit_cast(bf16x8, c);
     }
-    if (wave < 2) {  // per-row statistics: wave 0 lse2, wave 1 delta (rows past T clamped)
-      const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + h) * T;
-      const int i = min(i0 + lane, T - 1);
-      dma4(buf_desc(src, (unsigned)T * 4u), (unsigned)i * 4u, 0u, lds_u32(wave == 0 ? lse2_lds[buf] : dl_lds[buf]));
+#pragma unroll
+    for (int d = 0; d < ND; ++d) {
+      dk[d] = (f32x16){};
+      dv[d] = (f32x16){};
     }
-  };
-
-  // Copies run NBUF - 1 steps ahead. Vector memory operations complete in
-  // issue order, so the wait at the top of a step lets exactly the copies of
-  // the later steps already issued stay in flight.
-  const int dma_ops = 2 * QIPW + (wave < 2 ? 1 : 0);  // copies this wave issues per step
+    auto issue_step = [&](int step, int buf) {
+      const int hq = step / n_it;
+      const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
+      const int h = g * G + hq;
+      const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
+      const unsigned short* dop = (const unsigned short*)p.dout + (size_t)b * T * qrs + (size_t)h * D;
+      const BufDesc qrsr = buf_desc(qp, qspan), orsr = buf_desc(dop, qspan);
+      if (i0 + BWD_BM <= T) {
+        const unsigned so = (unsigned)i0 * qrs * 2u;
 #pragma unroll
-  for (int s = 0; s < NBUF - 1; ++s)
-    if (s < n_steps) issue_step(s, s);
-  auto step_fn = [&](int step, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
-    const int hq = step / n_it;
-    const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
-    wait_vmem_upto(dma_ops * (min(n_steps - 1, step + NBUF - 2) - step));
-    lds_barrier();  // this step's tiles landed everywhere; the oldest buffer is free
-    if (step + NBUF - 1 < n_steps) issue_step(step + NBUF - 1, (buf + NBUF - 1) % NBUF);
-    const bool any = (kw <= i0 + BWD_BM - 1) && (full || kw + 31 > i0 - win);
-    if (!any) return;
-    const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win) && (i0 + BWD_BM <= T);
-    const unsigned short* ql = q_lds[buf];
-    const unsigned short* ol = do_lds[buf];
-#pragma unroll
-    for (int ib = 0; ib < 2; ++ib) {
-      // Every LDS operand of this 32-query half is requested before the
-      // first product: q and dO rows (S, dP), the row statistics, and the
-      // dO^T / Q^T transpose reads (dV, dK).
-      bf16x8 aq[NS], ad[NS];
-#pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        aq[st] = *(const bf16x8*)(ql + aoff[st] + 32 * ib * D);
-        ad[st] = *(const bf16x8*)(ol + aoff[st] + 32 * ib * D);
-      }
-      f32x4 l4[4], d4[4];
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        l4[rg] = *(const f32x4*)(&lse2_lds[buf][32 * ib + 8 * rg + 4 * hh]);
-        d4[rg] = *(const f32x4*)(&dl_lds[buf][32 * ib + 8 * rg + 4 * hh]);
-      }
-      bf16x8 ot[2][ND], qt[2][ND];
-#pragma unroll
-      for (int u = 0; u < 2; ++u)
-#pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          const int rb = (32 * ib + 16 * u) * D;
-          ot[u][d] = cat_bf16x8(lds_read_tr16(ol + toff1[d] + rb), lds_read_tr16(ol + toff2[d] + rb));
-          qt[u][d] = cat_bf16x8(lds_read_tr16(ql + toff1[d] + rb), lds_read_tr16(ql + toff2[d] + rb));
+        for (int n = 0; n < QIPW; ++n) {
+          dma16(qrsr, ld_off[n], so, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
+          dma16(orsr, ld_off[n], so, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
         }
-
-      f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
+      } else {
 #pragma unroll
-      for (int st = 0; st < NS; ++st) {
-        sacc = mfma32(aq[st], kf[st], sacc);
-        dpacc = mfma32(ad[st], vf[st], dpacc);
+        for (int n = 0; n < QIPW; ++n) {
+          const int i = min(i0 + ld_row[n], T - 1);
+          const unsigned vo = (unsigned)(i * qrs + ld_ch[n] * 8) * 2u;
+          dma16(qrsr, vo, 0u, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
+          dma16(orsr, vo, 0u, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
+        }
       }
-      // sacc[r] = S[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][key kj]
-      unsigned pw[8], sw[8];  // P and dS as bf16 pairs
-      auto probs = [&](auto maskc) {
-        constexpr bool MASK = decltype(maskc)::value;
-        const int mbase = i0 + 32 * ib + 4 * hh - kj;
+      if (wave < 2) {  // per-row statistics: wave 0 lse2, wave 1 delta (rows past T clamped)
+        const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + h) * T;
+        const int i = min(i0 + lane, T - 1);
+        dma4(buf_desc(src, (unsigned)T * 4u), (unsigned)i * 4u, 0u, lds_u32(wave == 0 ? lse2_lds[buf] : dl_lds[buf]));
+      }
+    };
+
+    // Copies run NBUF - 1 steps ahead. Vector memory operations complete in
+    // issue order, so the wait at the top of a step lets exactly the copies of
+    // the later steps already issued stay in flight.
+    const int dma_ops = 2 * QIPW + (wave < 2 ? 1 : 0);  // copies this wave issues per step
+    auto step_fn = [&](int step, auto bufc) __attribute__((always_inline)) {
+      constexpr int buf = decltype(bufc)::value;
+      const int hq = step / n_it;
+      const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
+      wait_vmem_upto(dma_ops * (min(n_steps - 1, step + NBUF - 2) - step));
+      lds_barrier();  // this step's tiles landed everywhere; the oldest buffer is free
+      if (step + NBUF - 1 < n_steps) issue_step(step + NBUF - 1, (buf + NBUF - 1) % NBUF);
+      const bool any = (kw <= i0 + BWD_BM - 1) && (full || kw + 31 > i0 - win);
+      if (!any) return;
+      const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win) && (i0 + BWD_BM <= T);
+      const unsigned short* ql = q_lds[buf];
+      const unsigned short* ol = do_lds[buf];
+#pragma unroll
+      for (int ib = 0; ib < 2; ++ib) {
+        // Every LDS operand of this 32-query half is requested before the
+        // first product: q and dO rows (S, dP), the row statistics, and the
+        // dO^T / Q^T transpose reads (dV, dK).
+        bf16x8 aq[NS], ad[NS];
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          aq[st] = *(const bf16x8*)(ql + aoff[st] + 32 * ib * D);
+          ad[st] = *(const bf16x8*)(ol + aoff[st] + 32 * ib * D);
+        }
+        f32x4 l4[4], d4[4];
 #pragma unroll
         for (int rg = 0; rg < 4; ++rg) {
-          float pr[4], dsr[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rg + e;
-            float pv = exp2_fast(fmaf(sacc[r], p.scale_log2, -l4[rg][e]));
-            if (MASK) {
-              const int off = 8 * rg + e;
-              const bool vis = ((unsigned)(mbase + off) < wlim) && (i0 + 32 * ib + 8 * rg + 4 * hh + e < T);
-              pv = vis ? pv : 0.f;
-            }
-            pr[e] = pv;
-            dsr[e] = pv * (dpacc[r] - d4[rg][e]);
-          }
-          pw[2 * rg] = pk_bf16(pr[0], pr[1]);
-          pw[2 * rg + 1] = pk_bf16(pr[2], pr[3]);
-          sw[2 * rg] = pk_bf16(dsr[0], dsr[1]);
-          sw[2 * rg + 1] = pk_bf16(dsr[2], dsr[3]);
+          l4[rg] = *(const f32x4*)(&lse2_lds[buf][32 * ib + 8 * rg + 4 * hh]);
+          d4[rg] = *(const f32x4*)(&dl_lds[buf][32 * ib + 8 * rg + 4 * hh]);
         }
-      };
-      if (interior)
-        probs(std::integral_constant<bool, false>{});
-      else
-        probs(std::integral_constant<bool, true>{});
-      // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
+        bf16x8 ot[2][ND], qt[2][ND];
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 pq = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
-        const u32x4 sq = {sw[4 * u], sw[4 * u + 1], sw[4 * u + 2], sw[4 * u + 3]};
-        const bf16x8 pb = __builtin_bit_cast(bf16x8, pq);
-        const bf16x8 sb = __builtin_bit_cast(bf16x8, sq);
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int d = 0; d < ND; ++d) {
-          dv[d] = mfma32(ot[u][d], pb, dv[d]);
-          dk[d] = mfma32(qt[u][d], sb, dk[d]);
+          for (int d = 0; d < ND; ++d) {
+            const int rb = (32 * ib + 16 * u) * D;
+            ot[u][d] = cat_bf16x8(lds_read_tr16(ol + toff1[d] + rb), lds_read_tr16(ol + toff2[d] + rb));
+            qt[u][d] = cat_bf16x8(lds_read_tr16(ql + toff1[d] + rb), lds_read_tr16(ql + toff2[d] + rb));
+          }
+
+        f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
+#pragma unroll
+        for (int st = 0; st < NS; ++st) {
+          sacc = mfma32(aq[st], kf[st], sacc);
+          dpacc = mfma32(ad[st], vf[st], dpacc);
+        }
+        // sacc[r] = S[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][key kj]
+        unsigned pw[8], sw[8];  // P and dS as bf16 pairs
+        auto probs = [&](auto maskc) {
+          constexpr bool MASK = decltype(maskc)::value;
+          const int mbase = i0 + 32 * ib + 4 * hh - kj;
+#pragma unroll
+          for (int rg = 0; rg < 4; ++rg) {
+            float pr[4], dsr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rg + e;
+              float pv = exp2_fast(fmaf(sacc[r], p.scale_log2, -l4[rg][e]));
+              if (MASK) {
+                const int off = 8 * rg + e;
+                const bool vis = ((unsigned)(mbase + off) < wlim) && (i0 + 32 * ib + 8 * rg + 4 * hh + e < T);
+                pv = vis ? pv : 0.f;
+              }
+              pr[e] = pv;
+              dsr[e] = pv * (dpacc[r] - d4[rg][e]);
+            }
+            pw[2 * rg] = pk_bf16(pr[0], pr[1]);
+            pw[2 * rg + 1] = pk_bf16(pr[2], pr[3]);
+            sw[2 * rg] = pk_bf16(dsr[0], dsr[1]);
+            sw[2 * rg + 1] = pk_bf16(dsr[2], dsr[3]);
+          }
+        };
+        if (interior)
+          probs(std::integral_constant<bool, false>{});
+        else
+          probs(std::integral_constant<bool, true>{});
+        // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 pq = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+          const u32x4 sq = {sw[4 * u], sw[4 * u + 1], sw[4 * u + 2], sw[4 * u + 3]};
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, pq);
+          const bf16x8 sb = __builtin_bit_cast(bf16x8, sq);
+#pragma unroll
+          for (int d = 0; d < ND; ++d) {
+            dv[d] = mfma32(ot[u][d], pb, dv[d]);
+            dk[d] = mfma32(qt[u][d], sb, dk[d]);
+          }
         }
       }
+    };
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s)
+      if (s < n_steps) issue_step(s, s);
+    for (int step = 0; step < n_steps; step += NBUF) {
+      step_fn(step, std::integral_constant<int, 0>{});
+      if constexpr (NBUF > 1)
+        if (step + 1 < n_steps) step_fn(step + 1, std::integral_constant<int, 1 % NBUF>{});
+      if constexpr (NBUF > 2)
+        if (step + 2 < n_steps) step_fn(step + 2, std::integral_constant<int, 2 % NBUF>{});
+    }
+
+    // dK (scaled) and dV for this lane's key.
+    if (kj < T) {
+      unsigned short* dkp = (unsigned short*)p.dk + ((size_t)b * T + kj) * kvrs + (size_t)g * D;
+      unsigned short* dvp = (unsigned short*)p.dv + ((size_t)b * T + kj) * kvrs + (size_t)g * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          u32x2 wk, wv;
+          wk[0] = pk_bf16(dk[d][4 * rg] * p.scale, dk[d][4 * rg + 1] * p.scale);
+          wk[1] = pk_bf16(dk[d][4 * rg + 2] * p.scale, dk[d][4 * rg + 3] * p.scale);
+          wv[0] = pk_bf16(dv[d][4 * rg], dv[d][4 * rg + 1]);
+          wv[1] = pk_bf16(dv[d][4 * rg + 2], dv[d][4 * rg + 3]);
+          *(u32x2*)(dkp + 32 * d + 8 * rg + 4 * hh) = wk;
+          *(u32x2*)(dvp + 32 * d + 8 * rg + 4 * hh) = wv;
+        }
     }
   };
 
-  for (int step = 0; step < n_steps; step += NBUF) {
-    step_fn(step, std::integral_constant<int, 0>{});
-    if constexpr (NBUF > 1)
-      if (step + 1 < n_steps) step_fn(step + 1, std::integral_constant<int, 1 % NBUF>{});
-    if constexpr (NBUF > 2)
-      if (step + 2 < n_steps) step_fn(step + 2, std::integral_constant<int, 2 % NBUF>{});
-  }
-
-  // dK (scaled) and dV for this lane's key.
-  if (kj < T) {
-    unsigned short* dkp = (unsigned short*)p.dk + ((size_t)b * T + kj) * kvrs + (size_t)g * D;
-    unsigned short* dvp = (unsigned short*)p.dv + ((size_t)b * T + kj) * kvrs + (size_t)g * D;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        u32x2 wk, wv;
-        wk[0] = pk_bf16(dk[d][4 * rg] * p.scale, dk[d][4 * rg + 1] * p.scale);
-        wk[1] = pk_bf16(dk[d][4 * rg + 2] * p.scale, dk[d][4 * rg + 3] * p.scale);
-        wv[0] = pk_bf16(dv[d][4 * rg], dv[d][4 * rg + 1]);
-        wv[1] = pk_bf16(dv[d][4 * rg + 2], dv[d][4 * rg + 3]);
-        *(u32x2*)(dkp + 32 * d + 8 * rg + 4 * hh) = wk;
-        *(u32x2*)(dvp + 32 * d + 8 * rg + 4 * hh) = wv;
-      }
+  run(r_pair);
+  if (PAIRED && nkt - 1 - r_pair > r_pair) {
+    lds_barrier();  // every wave is done with the last step's tiles before they are reloaded
+    run(nkt - 1 - r_pair);
   }
 }
 
@@ -652,7 +662,10 @@ hipError_t launch_bf16(const BwdParams& p, hipStream_t s, const BwdEvents& ev) {
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record(ev.dkdv_begin, s)) != hipSuccess) return e;
   const int nkt = (p.T + BWD_BN - 1) / BWD_BN;
-  attn_bwd_dkdv_kernel<D><<<nkt * p.Hkv * p.B, BWD_THREADS, 0, s>>>(p);
+  if (p.window <= 0)
+    attn_bwd_dkdv_kernel<D, true><<<(nkt + 1) / 2 * p.Hkv * p.B, BWD_THREADS, 0, s>>>(p);
+  else
+    attn_bwd_dkdv_kernel<D, false><<<nkt * p.Hkv * p.B, BWD_THREADS, 0, s>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record(ev.end, s);
 }
