@@ -5,8 +5,9 @@ One step = one pass of the training-side hot path over one batch of the
 d20-shaped workload (B=32, T=2048, H=Hkv=10, D=128, bf16, 20 layers in the
 SSSL window schedule: 15 layers with a 1024-key window, 5 full causal):
 for every layer the QK prologue (RMSNorm + RoPE) forward and attention
-forward, then, in reverse layer order, attention backward and prologue
-backward. The reported value is band-counted attention fwd+bwd FLOPs
+forward, then, in reverse layer order, the backward through attention and
+the prologue (one call; the prologue backward is applied as the backward
+kernels store dq and dk). The reported value is band-counted attention fwd+bwd FLOPs
 (12 * D per visible query/key pair, per (b, h)) divided by the step time, so
 the prologue's time counts against it. The decode workload (64 rows, one
 query each, cache lengths uniform on 1..2048, same 20-layer schedule) is
@@ -122,7 +123,7 @@ def main():
     kp = [torch.empty_like(x) for x in kr]
     out = [torch.empty_like(x) for x in qr]
     lse = [torch.empty((B, H, T), dtype=torch.float32, device=dev) for _ in range(L)]
-    dqp, dkp, dv = torch.empty_like(qr[0]), torch.empty_like(kr[0]), torch.empty_like(vv[0])
+    dv = torch.empty_like(vv[0])
     dq, dk = torch.empty_like(qr[0]), torch.empty_like(kr[0])
     ws = torch.empty(native.nc_attn_bwd_workspace_bytes(native.NC_BF16, B, T, H, Hkv, D),
                      dtype=torch.uint8, device=dev)
@@ -151,15 +152,13 @@ def main():
                 tm.add("attn_bwd_dkdv", e1, e2)
                 native.nc_profile_bwd_main(e0, e1, e2)
             b and b.record()
-            native.nc_attn_bwd(qp[l], kp[l], vv[l], out[l], lse[l], do[l], wl.windows[l], scale,
-                               dq=dqp, dk=dkp, dv=dv, workspace=ws)
+            # attention backward and the prologue backward in one call: the
+            # backward kernels store dq, dk w.r.t. the raw q, k directly
+            native.nc_attn_bwd_prologue(qp[l], kp[l], vv[l], out[l], lse[l], do[l], wl.windows[l], scale,
+                                        qr[l], kr[l], cos, sin, eps, dq=dq, dk=dk, dv=dv, workspace=ws)
             e and e.record()
             if tm:
                 native.nc_profile_bwd_main()
-            b, e = ev("prologue_bwd")
-            b and b.record()
-            native.nc_qk_prologue_bwd(qr[l], kr[l], cos, sin, eps, dqp, dkp, dq=dq, dk=dk)
-            e and e.record()
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -269,7 +268,7 @@ def main():
         "data": "synthetic (seeded N(0,1) bf16, drawn on the device)",
         "config": {"workload": "d20_bf16: B=32 T=2048 H=Hkv=10 D=128, 20 layers SSSL "
                                "(15 x window 1024, 5 full causal); step = prologue fwd + attention fwd "
-                               "per layer, then attention bwd + prologue bwd per layer",
+                               "per layer, then the backward through attention and prologue per layer (one fused call)",
                    "B": B, "T": T, "H": H, "Hkv": Hkv, "D": D, "windows": wl.windows,
                    "band_flops_fwd": flops_f, "band_flops_bwd": flops_b},
         "attn_only_tflops": round((flops_f + flops_b) /

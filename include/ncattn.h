@@ -111,6 +111,28 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
                       void* workspace, size_t workspace_bytes, nc_stream stream);
 
 /*
+ * Backward through attention and the QK prologue in one call: the result of
+ * nc_attn_bwd followed by nc_qk_prologue_bwd, i.e. dq, dk are gradients
+ * w.r.t. the raw q_raw, k_raw ("nanochat Admin & Developer Guide", section 3:
+ * q and k are RMS-normalised and rotated before attention; the gradient
+ * passes back through both). q, k are the prologue outputs given to
+ * nc_attn_fwd; v, out, lse, dout, window, scale, workspace as for
+ * nc_attn_bwd; q_raw, k_raw, pos_offset, cos_tab, sin_tab, T_rope, eps as
+ * for nc_qk_prologue_bwd. For bf16 the prologue backward is applied by the
+ * backward kernels as they store dq and dk (the gradients w.r.t. q, k never
+ * reach memory). Outputs must not alias inputs. Validation and errors as for
+ * both calls it combines.
+ */
+nc_status nc_attn_bwd_prologue(nc_dtype dt, int B, int T, int H, int Hkv, int D,
+                               const void* q, const void* k, const void* v,
+                               const void* out, const float* lse, const void* dout,
+                               int window, float scale,
+                               const void* q_raw, const void* k_raw, const int32_t* pos_offset,
+                               const float* cos_tab, const float* sin_tab, int T_rope, float eps,
+                               void* dq, void* dk, void* dv,
+                               void* workspace, size_t workspace_bytes, nc_stream stream);
+
+/*
  * Measurement aid. While set on the calling thread, every nc_attn_bwd call
  * records, on its stream, dq_begin just before the kernel that forms dQ
  * (for bf16 it also forms the row statistics), dkdv_begin between it and
@@ -120,6 +142,7 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
  * Returns NC_ERR_INVALID_ARG unless all three or none are NULL.
  */
 nc_status nc_profile_bwd_main(void* dq_begin, void* dkdv_begin, void* end);
+/* (nc_attn_bwd_prologue records the same events.) */
 
 /*
  * Single-token decode against one layer's KV cache ("nanochat Admin &

@@ -182,3 +182,21 @@ def test_error_message_is_per_thread(L):
     t.join()
     assert seen == [""]
     assert "q is NULL" in msg(L)
+
+
+def bwdp(L, q_raw=A, k_raw=A, pos=None, T=64, T_rope=128, eps=1e-6, ws=A, wsb=1 << 30, dk=A, D=64):
+    return L.nc_attn_bwd_prologue(BF16, 1, T, 2, 1, D, A, A, A, A, A, A, 0, 0.1, q_raw, k_raw, pos, A, A,
+                                  T_rope, eps, A, dk, A, ws, wsb, None)
+
+
+def test_bwd_prologue_validation(L):
+    assert bwdp(L, q_raw=None) == INVALID
+    assert bwdp(L, k_raw=A + 4) == INVALID
+    assert bwdp(L, T_rope=32) == INVALID  # T > T_rope without offsets
+    assert "table" in msg(L)
+    assert bwdp(L, eps=-1.0) == INVALID
+    assert bwdp(L, pos=A + 2) == INVALID
+    assert bwdp(L, dk=None) == INVALID
+    assert bwdp(L, ws=None) == WORKSPACE
+    assert bwdp(L, wsb=16) == WORKSPACE
+    assert bwdp(L, D=80) == UNSUPPORTED

@@ -1,0 +1,105 @@
+"""GPU parity of nc_attn_bwd_prologue (backward through attention and the QK
+prologue in one call) against the fp64 oracle's composition of the two
+backward steps, through the C ABI: both dtypes, head dims 32/64/128 (the
+three ways the kernels pair d with d + D/2), windows, GQA, position
+offsets, ragged lengths, and d20 at full size on sampled batch rows."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import check, f64, inputs, rel_l2
+from transformer_attention_06_amd import synth
+from transformer_attention_06_amd.workload import FULL, workloads
+
+pytestmark = pytest.mark.gpu
+EPS = 2.0 ** -23
+
+
+def fused_case(native, B, T, H, Hkv, D, w, dtype, offsets, seed):
+    """Prologue fwd -> attention fwd -> fused backward on the GPU; the oracle
+    gets the GPU's prologue outputs for the attention part (so each kernel is
+    checked on its own inputs) and the raw q, k for the prologue part."""
+    import torch
+    scale = 1.0 / math.sqrt(D)
+    q, k, v, do = inputs([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D), (B, T, H, D)], seed, dtype)
+    c, s = native.nc_rope_table(4096, D)
+    offs = np.array([3, 900, 41][:B], np.int32) if offsets else None
+    po = torch.from_numpy(offs).cuda() if offsets else None
+    qp, kp = native.nc_qk_prologue_fwd(q, k, c, s, EPS, pos_offset=po)
+    out, lse = native.nc_attn_fwd(qp, kp, v, w, scale)
+    dq, dk, dv = native.nc_attn_bwd_prologue(qp, kp, v, out, lse, do, w, scale, q, k, c, s, EPS,
+                                             pos_offset=po)
+    torch.cuda.synchronize()
+    pos = oracle.positions_from_offsets(B, T, offs)
+    gqp, gkp, gv = oracle.attn_bwd(f64(qp), f64(kp), f64(v), f64(do), w, scale)
+    gq, gk = oracle.qk_prologue_bwd(f64(q), f64(k), pos, gqp, gkp, EPS)
+    tag = f"B{B} T{T} H{H} Hkv{Hkv} D{D} w{w} {dtype} offsets={offsets}"
+    check(tag + " dq", f64(dq), gq, dtype, "grad")
+    check(tag + " dk", f64(dk), gk, dtype, "grad")
+    check(tag + " dv", f64(dv), gv, dtype, "grad")
+    return q, k, v, do, qp, kp, out, lse, c, s, po, dq, dk, dv
+
+
+CASES = [
+    # B, T, H, Hkv, D, window, offsets
+    (1, 64, 2, 1, 32, 16, False),
+    (2, 130, 4, 2, 64, 0, True),
+    (1, 257, 4, 2, 128, 100, True),
+    (2, 200, 2, 2, 128, 0, False),
+    (3, 97, 6, 3, 32, 0, True),
+    (1, 300, 8, 2, 64, 129, False),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}T{}H{}Hkv{}D{}w{}o{}".format(*c))
+def test_fused_bwd_vs_oracle(gpu, dtype, case):
+    from transformer_attention_06_amd import native
+    print("case", dtype, case, flush=True)
+    B, T, H, Hkv, D, w, offsets = case
+    fused_case(native, B, T, H, Hkv, D, w, dtype, offsets, seed=900)
+
+
+def test_fused_matches_the_two_calls(gpu):
+    """bf16: the fused call and nc_attn_bwd followed by nc_qk_prologue_bwd
+    differ only by the bf16 rounding of the intermediate dq', dk'."""
+    from transformer_attention_06_amd import native
+    B, T, H, Hkv, D, w = 2, 260, 4, 2, 128, 0
+    q, k, v, do, qp, kp, out, lse, c, s, po, dq, dk, dv = fused_case(native, B, T, H, Hkv, D, w, "bf16",
+                                                                     True, 950)
+    dqp, dkp, dv2 = native.nc_attn_bwd(qp, kp, v, out, lse, do, w, 1.0 / math.sqrt(D))
+    dq2, dk2 = native.nc_qk_prologue_bwd(q, k, c, s, EPS, dqp, dkp, pos_offset=po)
+    assert rel_l2(f64(dv), f64(dv2)) == 0.0
+    assert rel_l2(f64(dq), f64(dq2)) < 5e-3
+    assert rel_l2(f64(dk), f64(dk2)) < 5e-3
+
+
+@pytest.mark.parametrize("w", [1024, FULL])
+def test_fused_d20_full_size_sampled_rows(gpu, w):
+    """d20 at full size in the bench's configuration (prologue positions
+    0..T-1), sampled batch rows against the oracle's composition."""
+    import torch
+    from transformer_attention_06_amd import native
+    wl = workloads()["d20_bf16"]
+    B, T, H, Hkv, D = wl.B, wl.T, wl.H, wl.Hkv, wl.D
+    seed = 1200 + w
+    q = synth.normal_device((B, T, H, D), seed, "bf16")
+    k = synth.normal_device((B, T, Hkv, D), seed + 1, "bf16")
+    v = synth.normal_device((B, T, Hkv, D), seed + 2, "bf16")
+    do = synth.normal_device((B, T, H, D), seed + 3, "bf16")
+    c, s = native.nc_rope_table(10 * T, D)
+    qp, kp = native.nc_qk_prologue_fwd(q, k, c, s, EPS)
+    out, lse = native.nc_attn_fwd(qp, kp, v, w, wl.scale)
+    dq, dk, dv = native.nc_attn_bwd_prologue(qp, kp, v, out, lse, do, w, wl.scale, q, k, c, s, EPS)
+    torch.cuda.synchronize()
+    rows = [0, B - 1]
+    print("d20 window", w, "rows", rows, flush=True)
+    pos = oracle.positions_from_offsets(len(rows), T)
+    gqp, gkp, gv = oracle.attn_bwd(f64(qp[rows]), f64(kp[rows]), f64(v[rows]), f64(do[rows]), w, wl.scale)
+    gq, gk = oracle.qk_prologue_bwd(f64(q[rows]), f64(k[rows]), pos, gqp, gkp, EPS)
+    check(f"d20 w{w} dq", f64(dq[rows]), gq, "bf16", "grad")
+    check(f"d20 w{w} dk", f64(dk[rows]), gk, "bf16", "grad")
+    check(f"d20 w{w} dv", f64(dv[rows]), gv, "bf16", "grad")

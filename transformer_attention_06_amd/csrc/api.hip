@@ -177,10 +177,55 @@ nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
   const size_t stat_bytes = ((size_t)B * H * T * 4 + 255) & ~(size_t)255;
   nc::BwdParams p{q, k, v, out, lse, dout, dq, dk, dv, (float*)workspace,
                   (float*)((char*)workspace + stat_bytes),
-                  B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f};
+                  B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f,
+                  nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0.f};
   hipStream_t s = (hipStream_t)stream;
   return finish(dt == NC_BF16 ? nc::launch_attn_bwd_bf16(p, s, g_bwd_ev) : nc::launch_attn_bwd_f32(p, s, g_bwd_ev),
                 s, "nc_attn_bwd");
+}
+
+static nc_status prologue_common(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
+                                 const int32_t* pos_offset, const float* cos_tab, const float* sin_tab,
+                                 int T_rope, float eps);
+
+nc_status nc_attn_bwd_prologue(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
+                               const void* v, const void* out, const float* lse, const void* dout, int window,
+                               float scale, const void* q_raw, const void* k_raw, const int32_t* pos_offset,
+                               const float* cos_tab, const float* sin_tab, int T_rope, float eps, void* dq,
+                               void* dk, void* dv, void* workspace, size_t workspace_bytes, nc_stream stream) {
+  NC_TRY(check_shape(dt, B, T, H, Hkv, D));
+  NC_TRY(check_ptr(q, "q"));
+  NC_TRY(check_ptr(k, "k"));
+  NC_TRY(check_ptr(v, "v"));
+  NC_TRY(check_ptr(out, "out"));
+  NC_TRY(check_ptr(lse, "lse"));
+  NC_TRY(check_ptr(dout, "dout"));
+  NC_TRY(check_ptr(dq, "dq"));
+  NC_TRY(check_ptr(dk, "dk"));
+  NC_TRY(check_ptr(dv, "dv"));
+  NC_TRY(check_scale(scale));
+  NC_TRY(prologue_common(dt, B, T, H, Hkv, D, q_raw, k_raw, pos_offset, cos_tab, sin_tab, T_rope, eps));
+  const size_t need = nc_attn_bwd_workspace_bytes(dt, B, T, H, Hkv, D);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+    return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  NC_TRY(check_device(nullptr));
+  const size_t stat_bytes = ((size_t)B * H * T * 4 + 255) & ~(size_t)255;
+  const bool bf16 = dt == NC_BF16;
+  // bf16: the two backward kernels apply the prologue backward before storing dq, dk.
+  // float32: attention gradients into dq, dk, then the prologue backward in place
+  // (each head vector is read whole before it is written).
+  nc::BwdParams p{q, k, v, out, lse, dout, dq, dk, dv, (float*)workspace,
+                  (float*)((char*)workspace + stat_bytes),
+                  B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f,
+                  bf16 ? q_raw : nullptr, bf16 ? k_raw : nullptr, pos_offset, cos_tab, sin_tab, T_rope, eps};
+  hipStream_t s = (hipStream_t)stream;
+  if (bf16) return finish(nc::launch_attn_bwd_bf16(p, s, g_bwd_ev), s, "nc_attn_bwd_prologue");
+  hipError_t e = nc::launch_attn_bwd_f32(p, s, g_bwd_ev);
+  if (e == hipSuccess) {
+    nc::PrologueParams pp{q_raw, k_raw, pos_offset, cos_tab, sin_tab, dq, dk, dq, dk, B, T, H, Hkv, D, T_rope, eps};
+    e = nc::launch_prologue(pp, false, true, s);
+  }
+  return finish(e, s, "nc_attn_bwd_prologue");
 }
 
 nc_status nc_profile_bwd_main(void* dq_begin, void* dkdv_begin, void* end) {

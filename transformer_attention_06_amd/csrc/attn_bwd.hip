@@ -52,6 +52,91 @@ constexpr int DQ_BM = 128;  // queries per dq workgroup (32 per wave)
 constexpr int DQ_BN = 64;   // keys per dq tile
 
 // --------------------------------------------------------------------------
+// Stores one head-vector gradient held in MFMA result layout: lane (li, hh)
+// holds g[db][4 rg + e] = dy[32 db + 8 rg + 4 hh + e] / mul, the lane with
+// the other hh the rest of the vector. Without the prologue the stored
+// values are dy; with it, the gradient w.r.t. the raw vector x at position
+// pos ("nanochat Admin & Developer Guide", section 3: weightless RMSNorm,
+// then half-split RoPE):
+//   u = R(-theta) dy,  r = sqrt(mean(x^2) + eps),  dx = u / r - x <x, u> / (D r^3).
+// All 64 lanes must call it (the row sums pair lanes l and l ^ 32); valid
+// says whether this lane's vector exists.
+template <int D>
+__device__ __forceinline__ void store_grad_row(const BwdParams& p, const f32x16* g, float mul, bool valid,
+                                               const unsigned short* xrow, int pos, int hh, unsigned short* orow) {
+  constexpr int ND = D / 32;
+  if (!xrow) {
+    if (valid) {
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int rg = 0; rg < 4; ++rg) {
+          u32x2 w;
+          w[0] = pk_bf16(g[d][4 * rg] * mul, g[d][4 * rg + 1] * mul);
+          w[1] = pk_bf16(g[d][4 * rg + 2] * mul, g[d][4 * rg + 3] * mul);
+          *(u32x2*)(orow + 32 * d + 8 * rg + 4 * hh) = w;
+        }
+    }
+    return;
+  }
+  const bool pos_ok = pos >= 0 && pos < p.T_rope;
+  const int tp = (valid && pos_ok) ? pos : 0;
+  float x[ND][16], u[ND][16];
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      u32x2 w = {0u, 0u};
+      if (valid) w = *(const u32x2*)(xrow + 32 * d + 8 * rg + 4 * hh);
+      x[d][4 * rg + 0] = __builtin_bit_cast(float, w[0] << 16);
+      x[d][4 * rg + 1] = __builtin_bit_cast(float, w[0] & 0xffff0000u);
+      x[d][4 * rg + 2] = __builtin_bit_cast(float, w[1] << 16);
+      x[d][4 * rg + 3] = __builtin_bit_cast(float, w[1] & 0xffff0000u);
+    }
+  // u = R(-theta) dy over the pairs (i, i + D/2): low a' = a c + b s, high b' = -a s + b c
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const bool low = ND >= 2 ? d < ND / 2 : rg < 2;
+      if (!low) continue;
+      const int pd = ND >= 2 ? d + ND / 2 : d, prg = ND >= 2 ? rg : rg + 2;
+      const int i = 32 * d + 8 * rg + 4 * hh;  // < D/2
+      const f32x4 c4 = *(const f32x4*)(p.cos_tab + (size_t)tp * (D / 2) + i);
+      const f32x4 s4 = *(const f32x4*)(p.sin_tab + (size_t)tp * (D / 2) + i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float a = g[d][4 * rg + e] * mul, b = g[pd][4 * prg + e] * mul;
+        u[d][4 * rg + e] = fmaf(a, c4[e], b * s4[e]);
+        u[pd][4 * prg + e] = fmaf(b, c4[e], -a * s4[e]);
+      }
+    }
+  float ss = 0.f, xu = 0.f;
+#pragma unroll
+  for (int d = 0; d < ND; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      ss = fmaf(x[d][e], x[d][e], ss);
+      xu = fmaf(x[d][e], u[d][e], xu);
+    }
+  ss = sum_mod<32>(ss);
+  xu = sum_mod<32>(xu);
+  const float inv_r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+  const float k3 = xu * inv_r * inv_r * inv_r * (1.0f / D);
+  if (valid) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = pos_ok ? fmaf(u[d][4 * rg + e], inv_r, -x[d][4 * rg + e] * k3) : NAN;
+        *(u32x2*)(orow + 32 * d + 8 * rg + 4 * hh) = (u32x2){pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3])};
+      }
+  }
+}
+
+// --------------------------------------------------------------------------
 // float32 path: delta = rowsum(dout * out), lse2 = lse * log2(e).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(BwdParams p) {
@@ -313,23 +398,11 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
         if (step + 2 < n_steps) step_fn(step + 2, std::integral_constant<int, 2 % NBUF>{});
     }
 
-    // dK (scaled) and dV for this lane's key.
-    if (kj < T) {
-      unsigned short* dkp = (unsigned short*)p.dk + ((size_t)b * T + kj) * kvrs + (size_t)g * D;
-      unsigned short* dvp = (unsigned short*)p.dv + ((size_t)b * T + kj) * kvrs + (size_t)g * D;
-#pragma unroll
-      for (int d = 0; d < ND; ++d)
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          u32x2 wk, wv;
-          wk[0] = pk_bf16(dk[d][4 * rg] * p.scale, dk[d][4 * rg + 1] * p.scale);
-          wk[1] = pk_bf16(dk[d][4 * rg + 2] * p.scale, dk[d][4 * rg + 3] * p.scale);
-          wv[0] = pk_bf16(dv[d][4 * rg], dv[d][4 * rg + 1]);
-          wv[1] = pk_bf16(dv[d][4 * rg + 2], dv[d][4 * rg + 3]);
-          *(u32x2*)(dkp + 32 * d + 8 * rg + 4 * hh) = wk;
-          *(u32x2*)(dvp + 32 * d + 8 * rg + 4 * hh) = wv;
-        }
-    }
+    // dV, and dK (scaled; through the prologue backward when asked) for this lane's key.
+    const size_t krow = ((size_t)b * T + kj) * kvrs + (size_t)g * D;
+    store_grad_row<D>(p, dv, 1.0f, kj < T, nullptr, 0, hh, (unsigned short*)p.dv + krow);
+    store_grad_row<D>(p, dk, p.scale, kj < T, p.k_raw ? (const unsigned short*)p.k_raw + krow : nullptr,
+                      kj + (p.pos_offset ? p.pos_offset[b] : 0), hh, (unsigned short*)p.dk + krow);
   };
 
   run(r_pair);
@@ -538,18 +611,10 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void attn_bwd_dq_kernel(BwdParams p
     if (jt + 1 <= t_end) tile(jt + 1, std::integral_constant<int, 1>{});
   }
 
-  if (q_valid) {
-    unsigned short* dqp = (unsigned short*)p.dq + ((size_t)b * T + qi) * qrs + (size_t)h * D;
-#pragma unroll
-    for (int d = 0; d < ND; ++d)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        u32x2 w;
-        w[0] = pk_bf16(acc[d][4 * rg] * p.scale, acc[d][4 * rg + 1] * p.scale);
-        w[1] = pk_bf16(acc[d][4 * rg + 2] * p.scale, acc[d][4 * rg + 3] * p.scale);
-        *(u32x2*)(dqp + 32 * d + 8 * rg + 4 * hh) = w;
-      }
-  }
+  // dq (through the prologue backward when asked) for this lane's query
+  const size_t qrow = ((size_t)b * T + qi) * qrs + (size_t)h * D;
+  store_grad_row<D>(p, acc, p.scale, q_valid, p.q_raw ? (const unsigned short*)p.q_raw + qrow : nullptr,
+                    qi + (p.pos_offset ? p.pos_offset[b] : 0), hh, (unsigned short*)p.dq + qrow);
 }
 
 // --------------------------------------------------------------------------

@@ -35,6 +35,15 @@ struct BwdParams {
   int window;
   float scale;
   float scale_log2;
+  // Optional QK prologue backward applied to dq and dk before they are
+  // stored (q_raw == nullptr: dq, dk are the gradients w.r.t. q, k).
+  const void* q_raw;
+  const void* k_raw;
+  const int32_t* pos_offset;  // device [B] or nullptr
+  const float* cos_tab;       // [T_rope, D/2]
+  const float* sin_tab;
+  int T_rope;
+  float eps;
 };
 
 struct DecodeParams {

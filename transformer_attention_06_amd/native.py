@@ -22,7 +22,8 @@ STATUS = {0: "NC_OK", 1: "NC_ERR_INVALID_ARG", 2: "NC_ERR_UNSUPPORTED", 3: "NC_E
 # every symbol include/ncattn.h declares
 EXPORTS = (
     "nc_abi_version", "nc_status_string", "nc_last_error_message",
-    "nc_attn_fwd", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd", "nc_profile_bwd_main",
+    "nc_attn_fwd", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd", "nc_attn_bwd_prologue",
+    "nc_profile_bwd_main",
     "nc_attn_decode_workspace_bytes", "nc_attn_decode",
     "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd",
 )
@@ -46,6 +47,8 @@ _SIGS = {
     "nc_attn_fwd": ([_i] * 6 + [_p, _p, _p, _i, _f, _p, _p, _p], _i),
     "nc_attn_bwd_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_bwd": ([_i] * 6 + [_p] * 6 + [_i, _f] + [_p] * 3 + [_p, _sz, _p], _i),
+    "nc_attn_bwd_prologue": ([_i] * 6 + [_p] * 6 + [_i, _f] + [_p] * 5 + [_i, _f] + [_p] * 3
+                             + [_p, _sz, _p], _i),
     "nc_profile_bwd_main": ([_p, _p, _p], _i),
     "nc_attn_decode_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_decode": ([_i] * 6 + [_p] * 4 + [_i, _f, _p, _p, _p, _sz, _p], _i),
@@ -146,6 +149,28 @@ def nc_attn_bwd(q, k, v, out, lse, dout, window, scale, dq=None, dk=None, dv=Non
                            _ptr(dout), int(window), float(scale), _ptr(dq), _ptr(dk), _ptr(dv),
                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     _raise_on("nc_attn_bwd", st)
+    return dq, dk, dv
+
+
+def nc_attn_bwd_prologue(q, k, v, out, lse, dout, window, scale, q_raw, k_raw, cos, sin, eps,
+                         pos_offset=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Backward through attention and the QK prologue: (dq, dk) w.r.t. the raw
+    q_raw, k_raw and dv, where q, k are the prologue outputs used in the forward."""
+    import torch
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    dq = _empty(q.shape, q) if dq is None else dq
+    dk = _empty(k.shape, k) if dk is None else dk
+    dv = _empty(v.shape, v) if dv is None else dv
+    need = nc_attn_bwd_workspace_bytes(_dt(q), B, T, H, Hkv, D)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().nc_attn_bwd_prologue(_dt(q), B, T, H, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                    _ptr(lse), _ptr(dout), int(window), float(scale), _ptr(q_raw),
+                                    _ptr(k_raw), _ptr(pos_offset), _ptr(cos), _ptr(sin), cos.shape[0],
+                                    float(eps), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _raise_on("nc_attn_bwd_prologue", st)
     return dq, dk, dv
 
 
