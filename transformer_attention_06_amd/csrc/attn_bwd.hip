@@ -60,12 +60,21 @@ constexpr int DQ_BN = 64;   // keys per dq tile
 // then half-split RoPE):
 //   u = R(-theta) dy,  r = sqrt(mean(x^2) + eps),  dx = u / r - x <x, u> / (D r^3).
 // All 64 lanes must call it (the row sums pair lanes l and l ^ 32); valid
-// says whether this lane's vector exists.
+// says whether this lane's vector exists. xw holds the lane's part of x as
+// loaded by load_row_words (nullptr: no prologue).
+template <int D>
+__device__ __forceinline__ void load_row_words(const unsigned short* xrow, bool valid, int hh, u32x2* xw) {
+#pragma unroll
+  for (int d = 0; d < D / 32; ++d)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg)
+      xw[4 * d + rg] = valid ? *(const u32x2*)(xrow + 32 * d + 8 * rg + 4 * hh) : (u32x2){0u, 0u};
+}
 template <int D>
 __device__ __forceinline__ void store_grad_row(const BwdParams& p, const f32x16* g, float mul, bool valid,
-                                               const unsigned short* xrow, int pos, int hh, unsigned short* orow) {
+                                               const u32x2* xw, int pos, int hh, unsigned short* orow) {
   constexpr int ND = D / 32;
-  if (!xrow) {
+  if (!xw) {
     if (valid) {
 #pragma unroll
       for (int d = 0; d < ND; ++d)
@@ -86,8 +95,7 @@ __device__ __forceinline__ void store_grad_row(const BwdParams& p, const f32x16*
   for (int d = 0; d < ND; ++d)
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      u32x2 w = {0u, 0u};
-      if (valid) w = *(const u32x2*)(xrow + 32 * d + 8 * rg + 4 * hh);
+      const u32x2 w = xw[4 * d + rg];
       x[d][4 * rg + 0] = __builtin_bit_cast(float, w[0] << 16);
       x[d][4 * rg + 1] = __builtin_bit_cast(float, w[0] & 0xffff0000u);
       x[d][4 * rg + 2] = __builtin_bit_cast(float, w[1] << 16);
@@ -242,6 +250,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
     const int j0 = kt * BWD_BN;
     const int kw = j0 + wave * 32;
     const int kj = kw + li;  // this lane's key
+    const size_t krow = ((size_t)b * T + kj) * kvrs + (size_t)g * D;  // its row of k, dk, dv
+    u32x2 xk[ND * 4];  // its raw k row (prologue backward), loaded during the last step
     const int i_last = full ? T - 1 : min(T - 1, j0 + BWD_BN - 1 + win - 1);
     const int it_begin = j0 / BWD_BM, n_it = i_last / BWD_BM - it_begin + 1;
     const int n_steps = G * n_it;
@@ -304,6 +314,8 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
       wait_vmem_upto(dma_ops * (min(n_steps - 1, step + NBUF - 2) - step));
       lds_barrier();  // this step's tiles landed everywhere; the oldest buffer is free
       if (step + NBUF - 1 < n_steps) issue_step(step + NBUF - 1, (buf + NBUF - 1) % NBUF);
+      // the raw k row for the prologue backward, requested during the last step
+      if (p.k_raw && step == n_steps - 1) load_row_words<D>((const unsigned short*)p.k_raw + krow, kj < T, hh, xk);
       const bool any = (kw <= i0 + BWD_BM - 1) && (full || kw + 31 > i0 - win);
       if (!any) return;
       const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win) && (i0 + BWD_BM <= T);
@@ -399,10 +411,9 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
     }
 
     // dV, and dK (scaled; through the prologue backward when asked) for this lane's key.
-    const size_t krow = ((size_t)b * T + kj) * kvrs + (size_t)g * D;
     store_grad_row<D>(p, dv, 1.0f, kj < T, nullptr, 0, hh, (unsigned short*)p.dv + krow);
-    store_grad_row<D>(p, dk, p.scale, kj < T, p.k_raw ? (const unsigned short*)p.k_raw + krow : nullptr,
-                      kj + (p.pos_offset ? p.pos_offset[b] : 0), hh, (unsigned short*)p.dk + krow);
+    store_grad_row<D>(p, dk, p.scale, kj < T, p.k_raw ? xk : nullptr, kj + (p.pos_offset ? p.pos_offset[b] : 0),
+                      hh, (unsigned short*)p.dk + krow);
   };
 
   run(r_pair);
@@ -611,10 +622,14 @@ __global__ __launch_bounds__(BWD_THREADS, 2) void attn_bwd_dq_kernel(BwdParams p
     if (jt + 1 <= t_end) tile(jt + 1, std::integral_constant<int, 1>{});
   }
 
-  // dq (through the prologue backward when asked) for this lane's query
+  // dq (through the prologue backward when asked) for this lane's query (its
+  // raw q row is loaded here: requesting it earlier costs registers the tile
+  // loop needs)
   const size_t qrow = ((size_t)b * T + qi) * qrs + (size_t)h * D;
-  store_grad_row<D>(p, acc, p.scale, q_valid, p.q_raw ? (const unsigned short*)p.q_raw + qrow : nullptr,
-                    qi + (p.pos_offset ? p.pos_offset[b] : 0), hh, (unsigned short*)p.dq + qrow);
+  u32x2 xq[ND * 4];
+  if (p.q_raw) load_row_words<D>((const unsigned short*)p.q_raw + qrow, q_valid, hh, xq);
+  store_grad_row<D>(p, acc, p.scale, q_valid, p.q_raw ? xq : nullptr, qi + (p.pos_offset ? p.pos_offset[b] : 0),
+                    hh, (unsigned short*)p.dq + qrow);
 }
 
 // --------------------------------------------------------------------------
