@@ -163,6 +163,8 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 template <int D, int G, bool BF16>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
   constexpr int CHUNK = decode_chunk(D, G);
+  constexpr int MAXS = 64;  // chunks staged at once (T_max / CHUNK beyond this loops)
+  __shared__ float sm[MAXS], sl[MAXS];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int L = p.seqlens[b];
   const size_t oi = ((size_t)b * p.H + h) * D + t;
@@ -178,14 +180,31 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
   const int lo = full ? 0 : L - p.window;
   const int s0 = lo / CHUNK, s1 = (L - 1) / CHUNK;
   const float* part = p.part + ((size_t)b * p.H + h) * p.n_split * (D + 2);
-  float M = -INFINITY;
-  for (int s = s0; s <= s1; ++s) M = fmaxf(M, part[(size_t)s * (D + 2) + D]);
-  float a = 0.f, z = 0.f;
-  for (int s = s0; s <= s1; ++s) {
-    const float* ps = part + (size_t)s * (D + 2);
-    const float f = exp2_fast(ps[D] - M);
-    a = fmaf(f, ps[t], a);
-    z = fmaf(f, ps[D + 1], z);
+  // The chunks' (m, l) are staged in LDS by one load per thread, so the
+  // merge does not wait for them one after another; each thread then sums
+  // its d over the chunks with independent loads.
+  float M = -INFINITY, a = 0.f, z = 0.f;
+  for (int c0 = s0; c0 <= s1; c0 += MAXS) {
+    const int nc = min(MAXS, s1 - c0 + 1);
+    __syncthreads();
+    if (t < nc) {
+      sm[t] = part[(size_t)(c0 + t) * (D + 2) + D];
+      sl[t] = part[(size_t)(c0 + t) * (D + 2) + D + 1];
+    }
+    __syncthreads();
+    float Mc = -INFINITY;
+    for (int i = 0; i < nc; ++i) Mc = fmaxf(Mc, sm[i]);
+    const float Mn = fmaxf(M, Mc);
+    const float r = exp2_fast(M - Mn);  // 0 on the first batch
+    a *= r;
+    z *= r;
+    M = Mn;
+#pragma unroll 8
+    for (int i = 0; i < nc; ++i) {
+      const float f = exp2_fast(sm[i] - M);
+      a = fmaf(f, part[(size_t)(c0 + i) * (D + 2) + t], a);
+      z = fmaf(f, sl[i], z);
+    }
   }
   const float o = a / z;
   if (BF16)
