@@ -17,7 +17,8 @@ Sources (titles and sections of the pages this follows):
     the SSSL sliding-window pattern; section 6 "Attention: FA3 with SDPA
     Fallback" (GQA via repeat-interleave of KV heads, single-token decode
     slicing the key window); section 7 "The Inference Engine & Tool Use",
-    "KV cache" (cache layout (B, T, H, D) per layer, int32 per-row lengths).
+    "KV cache" (cache layout (B, T, H, D) per layer, int32 per-row lengths,
+    in-place cache update, batch-1 prefill replicated to the sample rows).
   * "nanochat (Fucina port)", "Architecture": no-weight RMSNorm, half-split
     RoPE built from an inverse-frequency table, grouped causal attention.
 
@@ -42,4 +43,8 @@ from .prologue import (  # noqa: F401
     positions_from_offsets,
     qk_prologue_fwd,
     qk_prologue_bwd,
+)
+from .engine import (  # noqa: F401
+    decode_step,
+    kv_cache_replicate,
 )

@@ -1,0 +1,62 @@
+"""fp64 definition of the engine-side cache steps around single-token decode.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+  * Decode step with the cache updated in place. "nanochat Admin & Developer
+    Guide", section 7 "KV cache": the cache is built for FA3's kvcache call,
+    the position of each batch row is its int32 cache_seqlens entry, and the
+    cache is written in place; section 3: the new token's q and k go through
+    the QK prologue (weightless RMSNorm, then half-split RoPE) at that
+    position before attention. Reading of the pages: row b holds
+    n = cache_seqlens[b] tokens before the step; the new token is at
+    position n, its k' and v land in cache slot n, and the query attends to
+    slots max(0, n + 1 - w) .. n (the decode of oracle.attention with
+    L_b = n + 1). The lengths array itself is the caller's to advance.
+  * Cache replication. Section 7 "KV cache" and "Generation flow": the
+    prompt is prefilled once with batch 1 and that cache is copied to every
+    sample row. Only the prompt's positions are copied.
+"""
+
+import numpy as np
+
+from .attention import decode
+from .prologue import ROPE_BASE, qk_prologue_fwd
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window, scale, eps, base=ROPE_BASE):
+    """One decode step of one layer.
+
+    q [B, H, D], k_new, v_new [B, Hkv, D] (raw, before the prologue);
+    k_cache, v_cache [B, T_max, Hkv, D]; cache_seqlens [B] ints in
+    0 .. T_max - 1. Returns (out [B, H, D], lse [B, H], k_cache', v_cache')
+    where the returned caches are float64 copies with slot n of each row
+    replaced by the new token's k' and v; the inputs are not modified.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    B, H, D = q.shape
+    T_max = kc.shape[1]
+    n = np.asarray(cache_seqlens, dtype=np.int64)
+    if n.shape != (B,) or n.min() < 0 or n.max() >= T_max:
+        raise ValueError("cache_seqlens must be [B] with values in 0..T_max-1")
+    pos = n[:, None]  # [B, 1]: the new token's position
+    qp, kp = qk_prologue_fwd(q[:, None], k_new[:, None], pos, eps, base)
+    for b in range(B):
+        kc[b, n[b]] = kp[b, 0]
+        vc[b, n[b]] = v_new[b]
+    out, lse = decode(qp[:, 0], kc, vc, n + 1, window, scale)
+    return out, lse, kc, vc
+
+
+def kv_cache_replicate(src_row, n_rows, T_max, n_tokens):
+    """[n_rows, T_max, Hkv, D] float64 cache whose rows hold positions
+    0 .. n_tokens - 1 of src_row ([>= n_tokens, Hkv, D]); later positions are
+    NaN (their content is not defined by the step)."""
+    src = np.asarray(src_row, dtype=np.float64)
+    out = np.full((n_rows, T_max) + src.shape[1:], np.nan)
+    out[:, :n_tokens] = src[None, :n_tokens]
+    return out

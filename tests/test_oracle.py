@@ -283,6 +283,63 @@ def test_decode_matches_torch_fp64_sdpa():
         np.testing.assert_allclose(out[b], o[:, 0, :].numpy(), rtol=0, atol=1e-13)
 
 
+def test_decode_step_equals_last_row_of_prologue_prefill():
+    # A row's decode step over a cache filled by the prologue at positions 0..n-1
+    # is the last query row of a prefill of the raw n + 1 tokens: prologue at
+    # positions 0..n, then dense masked attention. Pins the new token's position
+    # (n), the slot it is written to and the window edge.
+    B, T_max, H, Hkv, D, eps = 3, 12, 4, 2, 8, 2.0 ** -23
+    lens = np.array([0, 5, 11])
+    for w in (0, 1, 3, 40):
+        qs, ks, vs = rnd((B, T_max, H, D), 60 + w), rnd((B, T_max, Hkv, D), 61 + w), rnd((B, T_max, Hkv, D), 62 + w)
+        pos = oracle.positions_from_offsets(B, T_max)
+        _, kp_all = oracle.qk_prologue_fwd(qs, ks, pos, eps)
+        kc = np.where(np.arange(T_max)[None, :, None, None] < lens[:, None, None, None], kp_all, np.nan)
+        vc = np.where(np.arange(T_max)[None, :, None, None] < lens[:, None, None, None], vs, np.nan)
+        idx = np.arange(B)
+        out, lse, kc2, vc2 = oracle.decode_step(qs[idx, lens], ks[idx, lens], vs[idx, lens], kc, vc, lens, w, 0.4, eps)
+        for b in range(B):
+            n = lens[b]
+            qp, kp = oracle.qk_prologue_fwd(qs[b:b + 1, :n + 1], ks[b:b + 1, :n + 1],
+                                            oracle.positions_from_offsets(1, n + 1), eps)
+            o, l = oracle.attn_fwd(qp, kp, vs[b:b + 1, :n + 1], w, 0.4)
+            np.testing.assert_allclose(out[b], o[0, n], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(lse[b], l[0, :, n], rtol=0, atol=1e-13)
+            # the cache gains exactly slot n; the slots before it are untouched
+            np.testing.assert_allclose(kc2[b, n], kp[0, n], rtol=0, atol=1e-15)
+            np.testing.assert_array_equal(vc2[b, n], vs[b, n])
+            np.testing.assert_array_equal(kc2[b, :n], kc[b, :n])
+            assert np.isnan(kc2[b, n + 1:]).all() and np.isnan(vc2[b, n + 1:]).all()
+
+
+def test_decode_step_at_position_zero_closed_form():
+    # n = 0: RoPE at position 0 is the identity, so q' and k' are the RMS-normalised
+    # raw vectors; one visible key gives out = v_new and lse = scale <q', k'>.
+    B, T_max, H, Hkv, D, eps = 2, 4, 4, 1, 16, 1e-6
+    q, k, v = rnd((B, H, D), 70), rnd((B, Hkv, D), 71), rnd((B, Hkv, D), 72)
+    kc, vc = rnd((B, T_max, Hkv, D), 73), rnd((B, T_max, Hkv, D), 74)
+    out, lse, kc2, vc2 = oracle.decode_step(q, k, v, kc, vc, np.zeros(B, int), 0, 0.25, eps)
+    for b in range(B):
+        kn = k[b, 0] / math.sqrt((k[b, 0] ** 2).mean() + eps)
+        np.testing.assert_allclose(kc2[b, 0, 0], kn, rtol=0, atol=1e-15)
+        for h in range(H):
+            qn = q[b, h] / math.sqrt((q[b, h] ** 2).mean() + eps)
+            np.testing.assert_allclose(out[b, h], v[b, 0], rtol=0, atol=1e-15)
+            np.testing.assert_allclose(lse[b, h], 0.25 * (qn @ kn), rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(kc2[:, 1:], kc[:, 1:])
+    with pytest.raises(ValueError):
+        oracle.decode_step(q, k, v, kc, vc, np.array([0, T_max]), 0, 0.25, eps)
+
+
+def test_kv_cache_replicate_copies_the_prompt_only():
+    src = rnd((9, 2, 4), 75)
+    out = oracle.kv_cache_replicate(src, 3, 12, 6)
+    assert out.shape == (3, 12, 2, 4)
+    for r in range(3):
+        np.testing.assert_array_equal(out[r, :6], src[:6])
+    assert np.isnan(out[:, 6:]).all()
+
+
 # ----------------------------------------------------------------------------
 # prologue
 
