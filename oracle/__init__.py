@@ -45,6 +45,7 @@ from .prologue import (  # noqa: F401
     qk_prologue_bwd,
 )
 from .engine import (  # noqa: F401
+    round_to,
     decode_step,
     kv_cache_replicate,
 )

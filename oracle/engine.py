@@ -13,6 +13,10 @@ product path.
     position n, its k' and v land in cache slot n, and the query attends to
     slots max(0, n + 1 - w) .. n (the decode of oracle.attention with
     L_b = n + 1). The lengths array itself is the caller's to advance.
+    The cache is storage of the model's dtype, so what the attention reads
+    back from slot n is k' as stored in that dtype: with cache_dtype "bf16"
+    (or "f32") the appended k' and v are rounded to it before the attention,
+    like every other cache entry; cache_dtype None keeps them exact.
   * Cache replication. Section 7 "KV cache" and "Generation flow": the
     prompt is prefilled once with batch 1 and that cache is copied to every
     sample row. Only the prompt's positions are copied.
@@ -24,7 +28,25 @@ from .attention import decode
 from .prologue import ROPE_BASE, qk_prologue_fwd
 
 
-def decode_step(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window, scale, eps, base=ROPE_BASE):
+def round_to(x, dtype):
+    """x rounded to the storage dtype: "f32" rounds to nearest even float32,
+    "bf16" to float32 and then to nearest even bfloat16 (8 significand bits);
+    None leaves x as it is. Returns float64."""
+    x = np.asarray(x, dtype=np.float64)
+    if dtype is None:
+        return x.copy()
+    f = x.astype(np.float32)
+    if dtype == "f32":
+        return f.astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError("dtype must be None, 'f32' or 'bf16'")
+    bits = f.view(np.uint32).astype(np.uint64)
+    bits = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
+    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window, scale, eps, base=ROPE_BASE,
+                cache_dtype=None):
     """One decode step of one layer.
 
     q [B, H, D], k_new, v_new [B, Hkv, D] (raw, before the prologue);
@@ -46,8 +68,8 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window, scale,
     pos = n[:, None]  # [B, 1]: the new token's position
     qp, kp = qk_prologue_fwd(q[:, None], k_new[:, None], pos, eps, base)
     for b in range(B):
-        kc[b, n[b]] = kp[b, 0]
-        vc[b, n[b]] = v_new[b]
+        kc[b, n[b]] = round_to(kp[b, 0], cache_dtype)
+        vc[b, n[b]] = round_to(v_new[b], cache_dtype)
     out, lse = decode(qp[:, 0], kc, vc, n + 1, window, scale)
     return out, lse, kc, vc
 

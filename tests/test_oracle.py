@@ -331,6 +331,38 @@ def test_decode_step_at_position_zero_closed_form():
         oracle.decode_step(q, k, v, kc, vc, np.array([0, T_max]), 0, 0.25, eps)
 
 
+def test_round_to_matches_torch_casts():
+    import torch
+    x = rnd((4096,), 76) * np.float64(3.0) ** rnd((4096,), 77)
+    # exact ties of bf16 (halfway between two bf16 values) in both directions
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(2.0 + 2.0 ** -7), 0.0, -0.0])
+    for v in (x, ties):
+        want = torch.from_numpy(v).float().to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(oracle.round_to(v, "bf16"), want)
+        np.testing.assert_array_equal(oracle.round_to(v, "f32"), torch.from_numpy(v).float().double().numpy())
+    np.testing.assert_array_equal(oracle.round_to(ties, None), ties)
+    assert oracle.round_to(np.array([1.0 + 2.0 ** -8]), "bf16")[0] == 1.0  # tie to even
+    assert oracle.round_to(np.array([1.0 + 3 * 2.0 ** -8]), "bf16")[0] == 1.0 + 2.0 ** -6
+
+
+def test_decode_step_stores_the_appended_key_in_the_cache_dtype():
+    B, T_max, H, Hkv, D, eps = 2, 6, 2, 1, 8, 1e-6
+    q, k, v = rnd((B, H, D), 78), rnd((B, Hkv, D), 79), rnd((B, Hkv, D), 80)
+    kc, vc = rnd((B, T_max, Hkv, D), 81), rnd((B, T_max, Hkv, D), 82)
+    n = np.array([2, 5])
+    o1, l1, k1, v1 = oracle.decode_step(q, k, v, kc, vc, n, 0, 0.3, eps)
+    o2, l2, k2, v2 = oracle.decode_step(q, k, v, kc, vc, n, 0, 0.3, eps, cache_dtype="bf16")
+    for b in range(B):
+        np.testing.assert_array_equal(k2[b, n[b]], oracle.round_to(k1[b, n[b]], "bf16"))
+        np.testing.assert_array_equal(v2[b, n[b]], oracle.round_to(v[b], "bf16"))
+    # the attention reads the stored values: same as a decode over the rounded cache
+    o3, l3 = oracle.decode(oracle.qk_prologue_fwd(q[:, None], k[:, None], n[:, None], eps)[0][:, 0], k2, v2, n + 1,
+                           0, 0.3)
+    np.testing.assert_allclose(o2, o3, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(l2, l3, rtol=0, atol=1e-15)
+    assert np.abs(o2 - o1).max() > 0
+
+
 def test_kv_cache_replicate_copies_the_prompt_only():
     src = rnd((9, 2, 4), 75)
     out = oracle.kv_cache_replicate(src, 3, 12, 6)
