@@ -167,6 +167,50 @@ nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max,
                          void* workspace, size_t workspace_bytes, nc_stream stream);
 
 /*
+ * One decode step of one layer with the cache updated in place, the way the
+ * pages describe the engine's use of FA3's kvcache call ("nanochat Admin &
+ * Developer Guide", section 7 "KV cache": the position of each row is its
+ * int32 cache_seqlens entry and the cache is written in place; section 3:
+ * the QK prologue, RMSNorm without weights then half-split RoPE).
+ * Row b holds n = cache_seqlens[b] cached tokens; the new token sits at
+ * position n:
+ *   q' = RoPE(RMSNorm(q[b]), n),  k' = RoPE(RMSNorm(k_new[b]), n)
+ *   k_cache[b, n] <- k',  v_cache[b, n] <- v_new[b]      (every kv head)
+ *   out[b], lse[b] = attention of q' over cache positions
+ *                    max(0, n + 1 - window) .. n        (window <= 0: all)
+ * exactly as nc_attn_decode with seqlens[b] = n + 1. cache_seqlens is a
+ * DEVICE int32 array [B] and is not modified (the caller advances it).
+ * A row with n outside 0..min(T_max, T_rope) - 1 leaves the cache untouched
+ * and gets NaN out and lse. Nothing else in the cache is written.
+ *   q [B,H,D], k_new/v_new [B,Hkv,D] (raw, before the prologue),
+ *   k_cache/v_cache [B,T_max,Hkv,D] (read and written), cos/sin [T_rope,D/2]
+ *   -> out [B,H,D], lse [B,H]
+ * k' is stored in the cache's dtype and the attention reads that stored
+ * value; q' is kept in float32. The inputs must not overlap the caches. The
+ * workspace (size from nc_attn_decode_step_workspace_bytes) holds the
+ * split-K partials, q' and the row key counts.
+ */
+size_t nc_attn_decode_step_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, int D, int T_max);
+nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_max,
+                              const void* q, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache, const int32_t* cache_seqlens,
+                              const float* cos_tab, const float* sin_tab, int T_rope, float eps,
+                              int window, float scale, void* out, float* lse,
+                              void* workspace, size_t workspace_bytes, nc_stream stream);
+
+/*
+ * Expands a batch-1 prefill cache into a decode cache of n_rows rows, so the
+ * prompt is processed once ("nanochat Admin & Developer Guide", section 7
+ * "KV cache" and "Generation flow": prefill once, then replicate the cache
+ * across the samples). Copies positions 0..n_tokens-1 of src (one row,
+ * position-major [>= n_tokens, Hkv, D]) into rows 0..n_rows-1 of
+ * dst [n_rows, T_max, Hkv, D]; later positions of dst are not written.
+ * Call once for k and once for v of each layer; src and dst must not overlap.
+ */
+nc_status nc_kv_cache_replicate(nc_dtype dt, int n_rows, int T_max, int Hkv, int D, int n_tokens,
+                                const void* src, void* dst, nc_stream stream);
+
+/*
  * RoPE table: cos_out[p, d] = cos(p * base^(-2d/D)), sin_out likewise, for
  * p in 0..T_rope-1 and d in 0..D/2-1, float32 [T_rope, D/2]. Angles and the
  * trigonometry are evaluated in float64 on the device, then rounded to

@@ -200,3 +200,47 @@ def test_bwd_prologue_validation(L):
     assert bwdp(L, ws=None) == WORKSPACE
     assert bwdp(L, wsb=16) == WORKSPACE
     assert bwdp(L, D=80) == UNSUPPORTED
+
+
+def test_decode_step_workspace_query_is_pure(L):
+    pad = lambda n: -(-n // 256) * 256  # noqa: E731
+    for dt in (BF16, F32):  # partials, q' (float32 whatever the dtype), row lengths
+        parts = L.nc_attn_decode_workspace_bytes(dt, 64, 10, 10, 128, 2048)
+        assert L.nc_attn_decode_step_workspace_bytes(dt, 64, 10, 10, 128, 2048) == \
+            pad(parts) + pad(64 * 10 * 128 * 4) + pad(64 * 4)
+    assert L.nc_attn_decode_step_workspace_bytes(BF16, 3, 4, 3, 32, 257) == 0
+
+
+def dstep(L, q=A, k_new=A, v_new=A, kc=A, vc=A, lens=A, cos=A, T_rope=128, eps=1e-6, lse=A, ws=A, wsb=1 << 30,
+          H=4, Hkv=2, D=64, scale=0.1):
+    return L.nc_attn_decode_step(BF16, 2, H, Hkv, D, 100, q, k_new, v_new, kc, vc, lens, cos, A, T_rope, eps, 0,
+                                 scale, A, lse, ws, wsb, None)
+
+
+def test_decode_step_validation(L):
+    assert dstep(L, H=5, Hkv=1) == UNSUPPORTED
+    assert dstep(L, D=96) == UNSUPPORTED
+    assert dstep(L, k_new=None) == INVALID
+    assert "k_new" in msg(L)
+    assert dstep(L, v_new=A + 8) == INVALID
+    assert dstep(L, kc=None) == INVALID
+    assert dstep(L, lens=None) == INVALID
+    assert dstep(L, lens=A + 2) == INVALID
+    assert dstep(L, cos=None) == INVALID
+    assert dstep(L, T_rope=0) == INVALID
+    assert dstep(L, eps=float("nan")) == INVALID
+    assert dstep(L, lse=A + 2) == INVALID
+    assert dstep(L, scale=0.0) == INVALID
+    assert dstep(L, ws=None) == WORKSPACE
+    assert dstep(L, wsb=100) == WORKSPACE
+
+
+def test_kv_cache_replicate_validation(L):
+    f = L.nc_kv_cache_replicate
+    assert f(BF16, 4, 100, 2, 64, 0, A, A, None) == INVALID  # n_tokens < 1
+    assert f(BF16, 4, 100, 2, 64, 101, A, A, None) == INVALID  # n_tokens > T_max
+    assert "n_tokens" in msg(L)
+    assert f(BF16, 4, 100, 2, 64, 10, None, A, None) == INVALID
+    assert f(BF16, 4, 100, 2, 64, 10, A, A + 4, None) == INVALID
+    assert f(BF16, 0, 100, 2, 64, 10, A, A, None) == INVALID
+    assert f(BF16, 4, 100, 2, 48, 10, A, A, None) == UNSUPPORTED

@@ -1,0 +1,134 @@
+"""GPU parity of nc_attn_decode_step (prologue + in-place cache append +
+split-K decode) and nc_kv_cache_replicate against the fp64 oracle, through
+the C ABI."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import check, f64, inputs
+from transformer_attention_06_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+EPS = 2.0 ** -23
+
+
+def _lens(B, T_max, seed):
+    n = synth.seqlens_np(B, T_max, seed) - 1  # tokens already cached: 0 .. T_max - 1
+    n[0], n[-1] = 0, T_max - 1
+    return n.astype(np.int32)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,H,Hkv,D,T_max,w", [
+    (8, 4, 4, 128, 300, 0), (8, 4, 4, 128, 300, 100), (5, 8, 2, 64, 700, 257),
+    (6, 6, 1, 32, 513, 0), (3, 8, 1, 128, 1024, 1), (4, 6, 2, 128, 256, 256)])
+def test_decode_step_parity_and_cache_writes(gpu, dtype, B, H, Hkv, D, T_max, w):
+    import torch
+    from transformer_attention_06_amd import native
+    print("case", B, H, Hkv, D, T_max, w, dtype, flush=True)
+    scale = 1.0 / math.sqrt(D)
+    q, kn, vn, kc, vc = inputs([(B, H, D), (B, Hkv, D), (B, Hkv, D), (B, T_max, Hkv, D), (B, T_max, Hkv, D)],
+                               400, dtype)
+    n = _lens(B, T_max, 401)
+    # poison the slots the step must neither read nor write: past the new
+    # token, and before the window of its query
+    for b, nb in enumerate(n):
+        kc[b, nb + 1:] = float("nan")
+        vc[b, nb + 1:] = float("nan")
+        if 0 < w <= nb:
+            kc[b, :nb + 1 - w] = float("nan")
+            vc[b, :nb + 1 - w] = float("nan")
+    kc0, vc0 = kc.clone(), vc.clone()
+    ro, rl, rkc, rvc = oracle.decode_step(f64(q), f64(kn), f64(vn), f64(kc), f64(vc), n, w, scale, EPS,
+                                          cache_dtype=dtype)
+    c, s = native.nc_rope_table(T_max, D)
+    out, lse = native.nc_attn_decode_step(q, kn, vn, kc, vc, torch.from_numpy(n).cuda(), c, s, EPS, w, scale)
+    check("decode_step out", f64(out), ro, dtype, "out")
+    check("decode_step lse", f64(lse), rl, dtype, "lse")
+    idx = torch.from_numpy(n.astype(np.int64)).cuda()
+    ar = torch.arange(B, device="cuda")
+    check("appended k'", f64(kc[ar, idx]), rkc[np.arange(B), n], dtype, "out")
+    assert torch.equal(vc[ar, idx], vn), "appended v must be the new v bit for bit"
+    # every other slot keeps its bits (NaN poison included)
+    keep = torch.ones((B, T_max), dtype=torch.bool, device="cuda")
+    keep[ar, idx] = False
+    for a, a0 in ((kc, kc0), (vc, vc0)):
+        x = a[keep].view(torch.int16 if dtype == "bf16" else torch.int32)
+        x0 = a0[keep].view(torch.int16 if dtype == "bf16" else torch.int32)
+        assert torch.equal(x, x0), "a cache slot other than the new token's changed"
+
+
+def test_decode_step_invalid_rows(gpu):
+    # n < 0, n >= T_max and n >= T_rope leave the row's cache alone and give NaN
+    import torch
+    from transformer_attention_06_amd import native
+    B, H, Hkv, D, T_max = 5, 4, 2, 64, 40
+    q, kn, vn, kc, vc = inputs([(B, H, D), (B, Hkv, D), (B, Hkv, D), (B, T_max, Hkv, D), (B, T_max, Hkv, D)],
+                               410, "bf16")
+    n = np.array([3, -1, 40, 30, 0], np.int32)
+    c, s = native.nc_rope_table(25, D)  # T_rope = 25 < T_max
+    kc0, vc0 = kc.clone(), vc.clone()
+    out, lse = native.nc_attn_decode_step(q, kn, vn, kc, vc, torch.from_numpy(n).cuda(), c, s, EPS, 0, 0.125)
+    good = [0, 4]
+    bad = [1, 2, 3]
+    assert torch.isfinite(out[good].float()).all() and torch.isfinite(lse[good]).all()
+    assert torch.isnan(out[bad].float()).all() and torch.isnan(lse[bad]).all()
+    assert torch.equal(kc[bad].view(torch.int16), kc0[bad].view(torch.int16))
+    assert torch.equal(vc[bad].view(torch.int16), vc0[bad].view(torch.int16))
+    ro, rl, _, _ = oracle.decode_step(f64(q)[good], f64(kn)[good], f64(vn)[good], f64(kc0)[good],
+                                      f64(vc0)[good], n[good], 0, 0.125, EPS, cache_dtype="bf16")
+    check("valid rows out", f64(out)[good], ro, "bf16", "out")
+    check("valid rows lse", f64(lse)[good], rl, "bf16", "lse")
+
+
+@pytest.mark.parametrize("w", [0, 5])
+def test_decode_steps_reproduce_prefill(gpu, w):
+    # a batch-1 prefill of the prompt, its cache replicated to B rows, then
+    # decode steps token by token: the last step equals the last row of an
+    # oracle prefill of the whole raw sequence
+    import torch
+    from transformer_attention_06_amd import native
+    B, H, Hkv, D, T_max, P, S = 3, 4, 2, 64, 64, 9, 6
+    scale = 1.0 / math.sqrt(D)
+    qs, ks, vs = inputs([(B, P + S, H, D), (B, P + S, Hkv, D), (B, P + S, Hkv, D)], 420, "bf16")
+    # every row shares the prompt (row 0's first P tokens)
+    for t in (qs, ks, vs):
+        t[1:, :P] = t[0:1, :P]
+    c, s = native.nc_rope_table(T_max, D)
+    _, kp = native.nc_qk_prologue_fwd(qs[:1, :P].contiguous(), ks[:1, :P].contiguous(), c, s, EPS)
+    kc = torch.full((B, T_max, Hkv, D), float("nan"), dtype=qs.dtype, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    native.nc_kv_cache_replicate(kp[0], kc, P)
+    native.nc_kv_cache_replicate(vs[0, :P].contiguous(), vc, P)
+    n = torch.full((B,), P, dtype=torch.int32, device="cuda")
+    for t in range(P, P + S):
+        out, lse = native.nc_attn_decode_step(qs[:, t].contiguous(), ks[:, t].contiguous(), vs[:, t].contiguous(),
+                                              kc, vc, n, c, s, EPS, w, scale)
+        n += 1
+    T = P + S
+    pos = oracle.positions_from_offsets(B, T)
+    rq, rk = oracle.qk_prologue_fwd(f64(qs), f64(ks), pos, EPS)
+    # every key is read back from the bf16 cache
+    ro, rl = oracle.attn_fwd(rq, oracle.round_to(rk, "bf16"), f64(vs), w, scale)
+    check("last step out", f64(out), ro[:, T - 1], "bf16", "out")
+    check("last step lse", f64(lse), rl[:, :, T - 1], "bf16", "lse")
+    check("cache k'", f64(kc[:, :T]), rk, "bf16", "out")
+    assert torch.equal(vc[:, :T], vs)
+    assert torch.isnan(kc[:, T:].float()).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kv_cache_replicate(gpu, dtype):
+    import torch
+    from transformer_attention_06_amd import native
+    n_rows, T_max, Hkv, D, n_tok = 7, 300, 3, 128, 257
+    src, = inputs([(T_max + 5, Hkv, D)], 430, dtype)
+    dst = torch.full((n_rows, T_max, Hkv, D), -7.0, dtype=src.dtype, device="cuda")
+    native.nc_kv_cache_replicate(src, dst, n_tok)
+    for r in range(n_rows):
+        assert torch.equal(dst[r, :n_tok], src[:n_tok])
+    assert (dst[:, n_tok:] == -7.0).all()

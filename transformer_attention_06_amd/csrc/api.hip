@@ -264,9 +264,81 @@ nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, c
     return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   NC_TRY(check_device(nullptr));
   nc::DecodeParams p{q, k_cache, v_cache, seqlens, out, lse, (float*)workspace, B, H, Hkv, D, T_max,
-                     window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), scale, scale * 1.4426950408889634f};
+                     window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), 0, scale,
+                     scale * 1.4426950408889634f};
   hipStream_t s = (hipStream_t)stream;
   return finish(nc::launch_decode(p, dt == NC_BF16, s), s, "nc_attn_decode");
+}
+
+static size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+size_t nc_attn_decode_step_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, int D, int T_max) {
+  const size_t parts = nc_attn_decode_workspace_bytes(dt, B, H, Hkv, D, T_max);
+  if (parts == 0) return 0;
+  return pad256(parts) + pad256((size_t)B * H * D * 4) + pad256((size_t)B * 4);  // partials, q' (f32), lengths
+}
+
+nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q,
+                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* cache_seqlens, const float* cos_tab, const float* sin_tab, int T_rope,
+                              float eps, int window, float scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, nc_stream stream) {
+  NC_TRY(check_shape(dt, B, T_max, H, Hkv, D));
+  if ((long long)B * T_max * Hkv * D > kMaxElems)
+    return fail(NC_ERR_UNSUPPORTED, "cache of B*T_max*Hkv*D elements exceeds 2^31-1");
+  if (!nc::decode_group_supported(H / Hkv))
+    return fail(NC_ERR_UNSUPPORTED, "decode supports query groups H/Hkv in {1,2,3,4,6,8}, got %d", H / Hkv);
+  NC_TRY(check_ptr(q, "q"));
+  NC_TRY(check_ptr(k_new, "k_new"));
+  NC_TRY(check_ptr(v_new, "v_new"));
+  NC_TRY(check_ptr(k_cache, "k_cache"));
+  NC_TRY(check_ptr(v_cache, "v_cache"));
+  if (!cache_seqlens) return fail(NC_ERR_INVALID_ARG, "cache_seqlens is NULL");
+  if (((uintptr_t)cache_seqlens & 3u) != 0) return fail(NC_ERR_INVALID_ARG, "cache_seqlens is not 4-byte aligned");
+  NC_TRY(check_ptr(cos_tab, "cos"));
+  NC_TRY(check_ptr(sin_tab, "sin"));
+  if (T_rope < 1) return fail(NC_ERR_INVALID_ARG, "T_rope must be >= 1");
+  if (!(eps >= 0.f) || !isfinite(eps)) return fail(NC_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  NC_TRY(check_ptr(out, "out"));
+  if (!lse) return fail(NC_ERR_INVALID_ARG, "lse is NULL");
+  if (((uintptr_t)lse & 3u) != 0) return fail(NC_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  NC_TRY(check_scale(scale));
+  const size_t need = nc_attn_decode_step_workspace_bytes(dt, B, H, Hkv, D, T_max);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+    return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  NC_TRY(check_device(nullptr));
+  char* ws = (char*)workspace;
+  float* parts = (float*)ws;
+  void* q_prime = ws + pad256(nc_attn_decode_workspace_bytes(dt, B, H, Hkv, D, T_max));
+  int32_t* lens = (int32_t*)((char*)q_prime + pad256((size_t)B * H * D * 4));
+  hipStream_t s = (hipStream_t)stream;
+  nc::AppendParams ap{q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos_tab, sin_tab, q_prime, lens,
+                      B, H, Hkv, D, T_max, T_rope, eps};
+  hipError_t e = nc::launch_decode_append(ap, dt == NC_BF16, s);
+  if (e == hipSuccess) {
+    nc::DecodeParams p{q_prime, k_cache, v_cache, lens, out, lse, parts, B, H, Hkv, D, T_max,
+                       window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), 1, scale,
+                       scale * 1.4426950408889634f};
+    e = nc::launch_decode(p, dt == NC_BF16, s);
+  }
+  return finish(e, s, "nc_attn_decode_step");
+}
+
+nc_status nc_kv_cache_replicate(nc_dtype dt, int n_rows, int T_max, int Hkv, int D, int n_tokens, const void* src,
+                                void* dst, nc_stream stream) {
+  NC_TRY(check_shape(dt, n_rows, T_max, Hkv, Hkv, D));
+  if ((long long)n_rows * T_max * Hkv * D > kMaxElems)
+    return fail(NC_ERR_UNSUPPORTED, "cache of n_rows*T_max*Hkv*D elements exceeds 2^31-1");
+  if (n_tokens < 1 || n_tokens > T_max)
+    return fail(NC_ERR_INVALID_ARG, "n_tokens=%d must lie in 1..T_max=%d", n_tokens, T_max);
+  NC_TRY(check_ptr(src, "src"));
+  NC_TRY(check_ptr(dst, "dst"));
+  NC_TRY(check_device(nullptr));
+  const size_t es = dt == NC_BF16 ? 2 : 4;
+  const size_t row_bytes = (size_t)Hkv * D * es;  // one cache position, a multiple of 16 bytes
+  hipStream_t s = (hipStream_t)stream;
+  return finish(nc::launch_replicate(src, dst, (size_t)n_tokens * row_bytes, n_rows, (size_t)T_max * row_bytes, s),
+                s, "nc_kv_cache_replicate");
 }
 
 nc_status nc_rope_table(int T_rope, int D, double base, float* cos_out, float* sin_out, nc_stream stream) {

@@ -22,6 +22,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -105,7 +107,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     float qf[8];
     {
       float t[8];
-      if (BF16)
+      if (BF16 && !p.q_f32)
         unpack8_bf16(*(const u32x4*)((const unsigned short*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8), t);
       else {
         const f32x4* pq = (const f32x4*)((const float*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8);
@@ -236,7 +238,25 @@ hipError_t launch_g(const DecodeParams& p, hipStream_t s) {
   }
 }
 
+// Batch-1 prefill cache row -> n_rows decode rows: 16-byte vectors, grid-stride.
+__global__ __launch_bounds__(256) void replicate_kernel(const u32x4* __restrict__ src, char* __restrict__ dst,
+                                                        size_t nvec, int n_rows, size_t row_stride) {
+  const size_t total = nvec * (size_t)n_rows;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = i / nvec, v = i - r * nvec;
+    *(u32x4*)(dst + r * row_stride + v * 16) = src[v];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_replicate(const void* src, void* dst, size_t n_bytes, int n_rows, size_t row_stride, hipStream_t s) {
+  const size_t nvec = n_bytes / 16;
+  const size_t total = nvec * (size_t)n_rows;
+  const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 8192);
+  replicate_kernel<<<blocks, 256, 0, s>>>((const u32x4*)src, (char*)dst, nvec, n_rows, row_stride);
+  return hipGetLastError();
+}
 
 bool decode_group_supported(int G) { return G == 1 || G == 2 || G == 3 || G == 4 || G == 6 || G == 8; }
 

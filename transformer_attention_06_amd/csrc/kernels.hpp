@@ -57,6 +57,7 @@ struct DecodeParams {
   int B, H, Hkv, D, T_max;
   int window;  // <= 0 full
   int n_split;
+  int q_f32;  // q is float32 whatever the cache dtype
   float scale;
   float scale_log2;
 };
@@ -72,6 +73,24 @@ struct PrologueParams {
   void* q_out;         // forward: q'; backward: dq
   void* k_out;         // forward: k'; backward: dk
   int B, T, H, Hkv, D, T_rope;
+  float eps;
+};
+
+// Decode step: forward prologue of the new token at position cache_seqlens[b],
+// its k' and v written into the cache there, q' and the key counts for the
+// decode kernels written to q_out and seqlens_out.
+struct AppendParams {
+  const void* q;      // [B, H, D] raw
+  const void* k_new;  // [B, Hkv, D] raw
+  const void* v_new;  // [B, Hkv, D]
+  void* k_cache;      // [B, T_max, Hkv, D]
+  void* v_cache;
+  const int32_t* cache_seqlens;  // [B] tokens already cached
+  const float* cos_tab;          // [T_rope, D/2]
+  const float* sin_tab;
+  void* q_out;           // [B, H, D] float32
+  int32_t* seqlens_out;  // [B] keys per row including the new token (0: row invalid)
+  int B, H, Hkv, D, T_max, T_rope;
   float eps;
 };
 
@@ -91,6 +110,9 @@ struct BwdEvents {
 hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s, const BwdEvents& ev);
 hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s, const BwdEvents& ev);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t s);
+hipError_t launch_decode_append(const AppendParams& p, bool bf16, hipStream_t s);
+// Copies the first n_bytes of src into n_rows rows of dst spaced row_stride bytes apart.
+hipError_t launch_replicate(const void* src, void* dst, size_t n_bytes, int n_rows, size_t row_stride, hipStream_t s);
 hipError_t launch_rope_table(int T_rope, int D, double base, float* c, float* sn, hipStream_t s);
 hipError_t launch_prologue(const PrologueParams& p, bool bf16, bool backward, hipStream_t s);
 

@@ -25,6 +25,7 @@ EXPORTS = (
     "nc_attn_fwd", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd", "nc_attn_bwd_prologue",
     "nc_profile_bwd_main",
     "nc_attn_decode_workspace_bytes", "nc_attn_decode",
+    "nc_attn_decode_step_workspace_bytes", "nc_attn_decode_step", "nc_kv_cache_replicate",
     "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd",
 )
 
@@ -52,6 +53,9 @@ _SIGS = {
     "nc_profile_bwd_main": ([_p, _p, _p], _i),
     "nc_attn_decode_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_decode": ([_i] * 6 + [_p] * 4 + [_i, _f, _p, _p, _p, _sz, _p], _i),
+    "nc_attn_decode_step_workspace_bytes": ([_i] * 6, _sz),
+    "nc_attn_decode_step": ([_i] * 6 + [_p] * 8 + [_i, _f, _i, _f, _p, _p, _p, _sz, _p], _i),
+    "nc_kv_cache_replicate": ([_i] * 6 + [_p, _p, _p], _i),
     "nc_rope_table": ([_i, _i, _d, _p, _p, _p], _i),
     "nc_qk_prologue_fwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p], _i),
     "nc_qk_prologue_bwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p, _p, _p], _i),
@@ -206,6 +210,46 @@ def nc_attn_decode(q, k_cache, v_cache, seqlens, window, scale, out=None, lse=No
                               _stream(stream))
     _raise_on("nc_attn_decode", st)
     return out, lse
+
+
+def nc_attn_decode_step_workspace_bytes(dtype_code, B, H, Hkv, D, T_max):
+    return lib().nc_attn_decode_step_workspace_bytes(dtype_code, B, H, Hkv, D, T_max)
+
+
+def nc_attn_decode_step(q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos, sin, eps, window, scale,
+                        out=None, lse=None, workspace=None, stream=None):
+    """Prologue of the new token at position cache_seqlens[b], k'/v_new written into the caches
+    there (in place), then decode over n + 1 keys. q [B,H,D], k_new/v_new [B,Hkv,D] raw,
+    caches [B,T_max,Hkv,D], cache_seqlens int32 [B] (device) -> (out [B,H,D], lse [B,H])."""
+    import torch
+    B, H, D = q.shape
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if cache_seqlens.dtype != torch.int32:
+        raise TypeError("cache_seqlens must be int32")
+    out = _empty(q.shape, q) if out is None else out
+    lse = _empty((B, H), q, torch.float32) if lse is None else lse
+    need = nc_attn_decode_step_workspace_bytes(_dt(q), B, H, Hkv, D, T_max)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().nc_attn_decode_step(_dt(q), B, H, Hkv, D, T_max, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_cache), _ptr(v_cache), _ptr(cache_seqlens), _ptr(cos), _ptr(sin),
+                                   cos.shape[0], float(eps), int(window), float(scale), _ptr(out), _ptr(lse),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream))
+    _raise_on("nc_attn_decode_step", st)
+    return out, lse
+
+
+def nc_kv_cache_replicate(src, dst, n_tokens, stream=None):
+    """Copies positions 0..n_tokens-1 of src (one cache row [>= n_tokens, Hkv, D], e.g. row 0 of a
+    batch-1 prefill cache) into every row of dst [n_rows, T_max, Hkv, D]."""
+    n_rows, T_max, Hkv, D = dst.shape
+    if src.dtype != dst.dtype or src.shape[-2:] != dst.shape[-2:] or src.numel() < n_tokens * Hkv * D:
+        raise ValueError("src must be one cache row of dst's dtype and [.., Hkv, D] shape")
+    st = lib().nc_kv_cache_replicate(_dt(dst), n_rows, T_max, Hkv, D, int(n_tokens), _ptr(src), _ptr(dst),
+                                     _stream(stream))
+    _raise_on("nc_kv_cache_replicate", st)
+    return dst
 
 
 def nc_rope_table(T_rope, D, base=100000.0, device="cuda", stream=None):
