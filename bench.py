@@ -101,7 +101,7 @@ def main():
 
     from transformer_attention_06_amd import native, synth
     from transformer_attention_06_amd.workload import (FULL, attn_flops, band_pairs, decode_bytes,
-                                                       workloads)
+                                                       decode_step_bytes, workloads)
 
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -240,6 +240,38 @@ def main():
                   "ms_per_step": round(dms, 4), "bytes_per_step": nbytes, "gbs": round(gbs, 1),
                   "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
         log("decode:", json.dumps(decode))
+
+        # decode step: the same caches and lengths with the token before the
+        # last appended in place (cache_seqlens = lens - 1), prologue included
+        kn_ = [synth.normal_device((DB, DHkv, DD), 2004 + 10 * l, "bf16") for l in range(len(dw.windows))]
+        vn_ = [synth.normal_device((DB, DHkv, DD), 2005 + 10 * l, "bf16") for l in range(len(dw.windows))]
+        csl = torch.from_numpy(lens - 1).to(dev)
+        dcos, dsin = native.nc_rope_table(Tm, DD)
+        sws = torch.empty(native.nc_attn_decode_step_workspace_bytes(native.NC_BF16, DB, DH, DHkv, DD, Tm),
+                          dtype=torch.uint8, device=dev)
+
+        def sstep():
+            for l, w in enumerate(dw.windows):
+                native.nc_attn_decode_step(dq_[l], kn_[l], vn_[l], kc[l], vc[l], csl, dcos, dsin, eps, w,
+                                           dw.scale, out=dout_, lse=dlse, workspace=sws)
+
+        for _ in range(args.warmup):
+            sstep()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            sstep()
+        t1.record()
+        torch.cuda.synchronize()
+        sms = t0.elapsed_time(t1) / args.steps
+        sbytes = sum(decode_step_bytes(lens - 1, DH, DHkv, DD, w) for w in dw.windows)
+        sgbs = sbytes / (sms * 1e-3) / 1e9
+        decode["step_with_append"] = {
+            "what": "nc_attn_decode_step per layer: prologue of the new token at position "
+                    "cache_seqlens[b] = L_b - 1, k'/v appended in place, split-K decode over L_b keys",
+            "ms_per_step": round(sms, 4), "bytes_per_step": sbytes, "gbs": round(sgbs, 1),
+            "frac_hbm_peak": round(sgbs / PEAK_HBM_GBS, 4)}
+        log("decode step:", json.dumps(decode["step_with_append"]))
         del kc, vc
 
     # ------------------------------------------------------------- roofline

@@ -61,3 +61,16 @@ def test_decode_bytes_brute_force():
             keys = [j for j in range(L) if w <= 0 or j >= L - w]
             total += len(keys) * Hkv * D * 2 * 2 + H * D * 2 * 2 + H * 4 + 4
         assert W.decode_bytes(lens, H, Hkv, D, w) == total
+
+
+def test_decode_step_bytes_brute_force():
+    rng = np.random.default_rng(1)
+    n_cached = rng.integers(0, 50, 17)
+    H, Hkv, D = 6, 2, 16
+    for w in (0, 1, 7, 60):
+        total = 0
+        for n in n_cached:
+            old = [j for j in range(n) if w <= 0 or j >= n + 1 - w]  # cached keys the query sees
+            total += len(old) * Hkv * D * 2 * 2 + Hkv * D * 2 * 2 + (H + 2 * Hkv) * D * 2
+            total += H * D * 2 + H * 4 + 4 + D * 4
+        assert W.decode_step_bytes(n_cached, H, Hkv, D, w) == total

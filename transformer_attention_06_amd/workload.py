@@ -69,6 +69,22 @@ def decode_bytes(seqlens, H, Hkv, D, window, elem_bytes=2):
     return total
 
 
+def decode_step_bytes(cache_seqlens, H, Hkv, D, window, elem_bytes=2):
+    """Algorithmic HBM bytes of one decode step (append + decode): the cached
+    keys the new query sees are read (K and V), the new k' and v are written
+    once, the raw q, k, v of the token are read, out and lse written, plus
+    the row's length and the cos/sin row of its position (float32)."""
+    total = 0
+    for n in cache_seqlens:
+        old = decode_keys(int(n) + 1, window) - 1  # visible keys other than the new one
+        total += 2 * Hkv * old * D * elem_bytes  # cached K and V rows read
+        total += 2 * Hkv * D * elem_bytes  # k', v written into the cache
+        total += (H + 2 * Hkv) * D * elem_bytes  # raw q, k, v read
+        total += H * D * elem_bytes + H * 4 + 4  # out, lse, length
+        total += D * 4  # cos and sin rows (D/2 each)
+    return total
+
+
 @dataclass
 class Workload:
     name: str
