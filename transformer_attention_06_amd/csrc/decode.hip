@@ -19,6 +19,8 @@
 //   Chunks outside a row's key range exit without reading anything.
 // decode_combine: merges a row's partials into out and lse. A length outside
 //   1..T_max yields NaN out and lse for that row.
+// replicate: copies a batch-1 prompt cache row into every decode row (section
+//   7: the prompt is prefilled once and its cache copied to the samples).
 
 #include <math.h>
 
