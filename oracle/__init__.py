@@ -48,4 +48,6 @@ from .engine import (  # noqa: F401
     round_to,
     decode_step,
     kv_cache_replicate,
+    cache_append,
+    prefill_chunk,
 )

@@ -20,6 +20,14 @@ product path.
   * Cache replication. Section 7 "KV cache" and "Generation flow": the
     prompt is prefilled once with batch 1 and that cache is copied to every
     sample row. Only the prompt's positions are copied.
+  * Chunked prefill against a cache. Section 6: the SDPA fallback's third
+    case, chunked / sliding-window inference, where the queries of a chunk
+    are fewer than the keys and the visible keys form a shifted causal
+    (optionally windowed) band built as an explicit mask. Reading: row b has
+    n_b = cache_seqlens[b] tokens cached; the chunk's Tq tokens sit at
+    positions n_b .. n_b + Tq - 1, their k and v already written to those
+    cache slots (cache_append); chunk query t attends to cache slots j with
+    p - w < j <= p, p = n_b + t (all j <= p for a full layer).
 """
 
 import numpy as np
@@ -82,3 +90,59 @@ def kv_cache_replicate(src_row, n_rows, T_max, n_tokens):
     out = np.full((n_rows, T_max) + src.shape[1:], np.nan)
     out[:, :n_tokens] = src[None, :n_tokens]
     return out
+
+
+def cache_append(k_chunk, v_chunk, k_cache, v_cache, cache_seqlens, cache_dtype=None):
+    """Copies of the caches with the chunk's k, v [B, Tq, Hkv, D] written at
+    slots n_b .. n_b + Tq - 1 of each row (rounded to the cache dtype)."""
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    k_chunk = np.asarray(k_chunk, dtype=np.float64)
+    v_chunk = np.asarray(v_chunk, dtype=np.float64)
+    B, Tq = k_chunk.shape[:2]
+    n = np.asarray(cache_seqlens, dtype=np.int64)
+    if n.shape != (B,) or n.min() < 0 or (n + Tq).max() > kc.shape[1]:
+        raise ValueError("every row needs 0 <= n_b and n_b + Tq <= T_max")
+    for b in range(B):
+        kc[b, n[b]:n[b] + Tq] = round_to(k_chunk[b], cache_dtype)
+        vc[b, n[b]:n[b] + Tq] = round_to(v_chunk[b], cache_dtype)
+    return kc, vc
+
+
+def prefill_chunk(q, k_cache, v_cache, cache_seqlens, window, scale):
+    """Attention of a chunk of queries against a cache that already holds the
+    chunk's own keys.
+
+    q [B, Tq, H, D]; k_cache, v_cache [B, T_max, Hkv, D]; cache_seqlens [B]
+    with 0 <= n_b and n_b + Tq <= T_max. Query t of row b sits at position
+    p = n_b + t and sees slots j with p - w < j <= p (w <= 0: all j <= p).
+    Returns out [B, Tq, H, D] and lse [B, H, Tq]. Dense masked scores.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    B, Tq, H, D = q.shape
+    T_max, Hkv = kc.shape[1], kc.shape[2]
+    n = np.asarray(cache_seqlens, dtype=np.int64)
+    if n.shape != (B,) or n.min() < 0 or (n + Tq).max() > T_max:
+        raise ValueError("every row needs 0 <= n_b and n_b + Tq <= T_max")
+    G = H // Hkv
+    out = np.zeros((B, Tq, H, D))
+    lse = np.zeros((B, H, Tq))
+    for b in range(B):
+        Lk = int(n[b]) + Tq  # slots 0 .. Lk - 1 hold keys
+        p = n[b] + np.arange(Tq)[:, None]
+        j = np.arange(Lk)[None, :]
+        vis = j <= p
+        if window > 0:
+            vis &= j > p - window
+        for h in range(H):
+            g = h // G
+            s = scale * (q[b, :, h, :] @ kc[b, :Lk, g, :].T)
+            s = np.where(vis, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            e = np.exp(s - m)
+            z = e.sum(axis=1, keepdims=True)
+            out[b, :, h, :] = (e / z) @ vc[b, :Lk, g, :]
+            lse[b, h, :] = (m + np.log(z))[:, 0]
+    return out, lse

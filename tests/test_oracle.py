@@ -372,6 +372,72 @@ def test_kv_cache_replicate_copies_the_prompt_only():
     assert np.isnan(out[:, 6:]).all()
 
 
+def test_prefill_chunk_equals_rows_of_a_full_prefill():
+    # a chunk after n_b cached tokens is rows n_b .. n_b + Tq - 1 of the plain
+    # prefill of all n_b + Tq tokens (n_b = 0 is the prefill itself)
+    B, Tq, T_max, H, Hkv, D = 3, 5, 20, 4, 2, 8
+    n = np.array([0, 6, 15])
+    qf, kf, vf = rnd((B, T_max, H, D), 90), rnd((B, T_max, Hkv, D), 91), rnd((B, T_max, Hkv, D), 92)
+    for w in (0, 1, 4, 9, 50):
+        q = np.stack([qf[b, n[b]:n[b] + Tq] for b in range(B)])
+        out, lse = oracle.prefill_chunk(q, kf, vf, n, w, 0.35)
+        for b in range(B):
+            L = n[b] + Tq
+            o, l = oracle.attn_fwd(qf[b:b + 1, :L], kf[b:b + 1, :L], vf[b:b + 1, :L], w, 0.35)
+            np.testing.assert_allclose(out[b], o[0, n[b]:L], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(lse[b], l[0, :, n[b]:L], rtol=0, atol=1e-13)
+
+
+def test_prefill_chunk_of_one_token_is_decode():
+    B, T_max, H, Hkv, D = 4, 16, 6, 3, 8
+    kc, vc = rnd((B, T_max, Hkv, D), 93), rnd((B, T_max, Hkv, D), 94)
+    q = rnd((B, 1, H, D), 95)
+    n = np.array([0, 3, 9, 15])
+    for w in (0, 2, 7):
+        out, lse = oracle.prefill_chunk(q, kc, vc, n, w, 0.5)
+        od, ld = oracle.decode(q[:, 0], kc, vc, n + 1, w, 0.5)
+        np.testing.assert_allclose(out[:, 0], od, rtol=0, atol=1e-14)
+        np.testing.assert_allclose(lse[:, :, 0], ld, rtol=0, atol=1e-14)
+
+
+def test_prefill_chunk_matches_torch_fp64_sdpa_with_explicit_mask():
+    import torch
+    import torch.nn.functional as F
+    B, Tq, T_max, H, Hkv, D = 2, 7, 24, 4, 1, 16
+    kc, vc = rnd((B, T_max, Hkv, D), 96), rnd((B, T_max, Hkv, D), 97)
+    q = rnd((B, Tq, H, D), 98)
+    n = np.array([4, 17])
+    w = 6
+    out, _ = oracle.prefill_chunk(q, kc, vc, n, w, 0.25)
+    for b in range(B):
+        L = n[b] + Tq
+        p = n[b] + np.arange(Tq)[:, None]
+        j = np.arange(L)[None, :]
+        mask = torch.from_numpy((j <= p) & (j > p - w))
+        o = F.scaled_dot_product_attention(
+            torch.from_numpy(q[b]).permute(1, 0, 2), torch.from_numpy(kc[b, :L]).permute(1, 0, 2),
+            torch.from_numpy(vc[b, :L]).permute(1, 0, 2), attn_mask=mask, scale=0.25, enable_gqa=True)
+        np.testing.assert_allclose(out[b], o.permute(1, 0, 2).numpy(), rtol=0, atol=1e-13)
+
+
+def test_cache_append_writes_the_chunk_slots_only():
+    B, Tq, T_max, Hkv, D = 2, 3, 10, 2, 4
+    kc, vc = rnd((B, T_max, Hkv, D), 99), rnd((B, T_max, Hkv, D), 100)
+    kn, vn = rnd((B, Tq, Hkv, D), 101), rnd((B, Tq, Hkv, D), 102)
+    n = np.array([0, 7])
+    k2, v2 = oracle.cache_append(kn, vn, kc, vc, n)
+    for b in range(B):
+        sl = slice(n[b], n[b] + Tq)
+        np.testing.assert_array_equal(k2[b, sl], kn[b])
+        np.testing.assert_array_equal(v2[b, sl], vn[b])
+        keep = np.ones(T_max, bool)
+        keep[sl] = False
+        np.testing.assert_array_equal(k2[b, keep], kc[b, keep])
+        np.testing.assert_array_equal(v2[b, keep], vc[b, keep])
+    with pytest.raises(ValueError):
+        oracle.cache_append(kn, vn, kc, vc, np.array([0, 8]))
+
+
 # ----------------------------------------------------------------------------
 # prologue
 
