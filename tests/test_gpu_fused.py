@@ -19,9 +19,9 @@ EPS = 2.0 ** -23
 
 
 def fused_case(native, B, T, H, Hkv, D, w, dtype, offsets, seed):
-    """Prologue fwd -> attention fwd -> fused backward on the GPU; the oracle
-    gets the GPU's prologue outputs for the attention part (so each kernel is
-    checked on its own inputs) and the raw q, k for the prologue part."""
+    """Prologue fwd -> attention fwd -> fused backward on the GPU against the
+    oracle's composition from the raw inputs: its prologue outputs are stored
+    in the model dtype (round_to), as the GPU's are, before its attention."""
     import torch
     scale = 1.0 / math.sqrt(D)
     q, k, v, do = inputs([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D), (B, T, H, D)], seed, dtype)
@@ -34,7 +34,8 @@ def fused_case(native, B, T, H, Hkv, D, w, dtype, offsets, seed):
                                              pos_offset=po)
     torch.cuda.synchronize()
     pos = oracle.positions_from_offsets(B, T, offs)
-    gqp, gkp, gv = oracle.attn_bwd(f64(qp), f64(kp), f64(v), f64(do), w, scale)
+    rq, rk = (oracle.round_to(x, dtype) for x in oracle.qk_prologue_fwd(f64(q), f64(k), pos, EPS))
+    gqp, gkp, gv = oracle.attn_bwd(rq, rk, f64(v), f64(do), w, scale)
     gq, gk = oracle.qk_prologue_bwd(f64(q), f64(k), pos, gqp, gkp, EPS)
     tag = f"B{B} T{T} H{H} Hkv{Hkv} D{D} w{w} {dtype} offsets={offsets}"
     check(tag + " dq", f64(dq), gq, dtype, "grad")
@@ -98,7 +99,8 @@ def test_fused_d20_full_size_sampled_rows(gpu, w):
     rows = [0, B - 1]
     print("d20 window", w, "rows", rows, flush=True)
     pos = oracle.positions_from_offsets(len(rows), T)
-    gqp, gkp, gv = oracle.attn_bwd(f64(qp[rows]), f64(kp[rows]), f64(v[rows]), f64(do[rows]), w, wl.scale)
+    rq, rk = (oracle.round_to(x, "bf16") for x in oracle.qk_prologue_fwd(f64(q[rows]), f64(k[rows]), pos, EPS))
+    gqp, gkp, gv = oracle.attn_bwd(rq, rk, f64(v[rows]), f64(do[rows]), w, wl.scale)
     gq, gk = oracle.qk_prologue_bwd(f64(q[rows]), f64(k[rows]), pos, gqp, gkp, EPS)
     check(f"d20 w{w} dq", f64(dq[rows]), gq, "bf16", "grad")
     check(f"d20 w{w} dk", f64(dk[rows]), gk, "bf16", "grad")
