@@ -88,6 +88,40 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
                       void* out, float* lse, nc_stream stream);
 
 /*
+ * A chunk of Tq queries per row against a KV cache: the SDPA fallback's
+ * chunked-inference case ("nanochat Admin & Developer Guide", section 6: the
+ * queries are fewer than the keys and the visible keys are a shifted causal,
+ * optionally windowed, band; section 7 "KV cache": per-row int32
+ * cache_seqlens). Row b holds n = cache_seqlens[b] tokens before the chunk;
+ * the chunk's keys and values must already be in cache slots n .. n + Tq - 1
+ * (nc_kv_cache_append). Chunk query t sits at position p = n + t and sees
+ * slots j with p - window < j <= p (window <= 0: all j <= p):
+ *   lse[b,h,t] = ln sum_j exp(s_tj),  out[b,t,h] = sum_j exp(s_tj - lse) v_j,
+ *   s_tj = scale * <q[b,t,h], k_cache[b,j,g]>.
+ * Same kernels and numerics as nc_attn_fwd (which is this call with n = 0,
+ * Tq = T_max = T). cache_seqlens is a DEVICE int32 array [B]; a row with
+ * n < 0 or n + Tq > T_max gets NaN out and lse.
+ *   q [B,Tq,H,D] (after the prologue, e.g. nc_qk_prologue_fwd with
+ *   pos_offset = cache_seqlens), k_cache/v_cache [B,T_max,Hkv,D]
+ *   -> out [B,Tq,H,D], lse [B,H,Tq]
+ */
+nc_status nc_attn_fwd_cache(nc_dtype dt, int B, int Tq, int H, int Hkv, int D, int T_max,
+                            const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* cache_seqlens, int window, float scale,
+                            void* out, float* lse, nc_stream stream);
+
+/*
+ * Writes a chunk's keys and values into the cache in place (section 7 "KV
+ * cache"): k_cache[b, n + t] <- k_new[b, t], v_cache[b, n + t] <- v_new[b, t]
+ * for t < Tq, n = cache_seqlens[b] (DEVICE int32 [B], not modified). A row
+ * with n < 0 or n + Tq > T_max is left untouched. Nothing else is written.
+ *   k_new/v_new [B,Tq,Hkv,D] -> k_cache/v_cache [B,T_max,Hkv,D]
+ */
+nc_status nc_kv_cache_append(nc_dtype dt, int B, int Tq, int Hkv, int D, int T_max,
+                             const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                             const int32_t* cache_seqlens, nc_stream stream);
+
+/*
  * Attention backward: gradients of L = sum(out * dout) w.r.t. q, k, v, with
  * P recomputed from the saved lse. Per (b, h):
  *   dP_ij = <dout_i, v_j>, delta_i = <dout_i, out_i>,

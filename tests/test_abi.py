@@ -244,3 +244,32 @@ def test_kv_cache_replicate_validation(L):
     assert f(BF16, 4, 100, 2, 64, 10, A, A + 4, None) == INVALID
     assert f(BF16, 0, 100, 2, 64, 10, A, A, None) == INVALID
     assert f(BF16, 4, 100, 2, 48, 10, A, A, None) == UNSUPPORTED
+
+
+def fcache(L, q=A, kc=A, lens=A, out=A, lse=A, Tq=8, T_max=64, H=4, Hkv=2, D=64, scale=0.1):
+    return L.nc_attn_fwd_cache(BF16, 2, Tq, H, Hkv, D, T_max, q, kc, A, lens, 0, scale, out, lse, None)
+
+
+def test_fwd_cache_validation(L):
+    assert fcache(L, T_max=7) == INVALID
+    assert "T_max" in msg(L)
+    assert fcache(L, H=3) == INVALID
+    assert fcache(L, D=96) == UNSUPPORTED
+    assert fcache(L, q=None) == INVALID
+    assert fcache(L, kc=A + 2) == INVALID
+    assert fcache(L, lens=None) == INVALID
+    assert fcache(L, lens=A + 1) == INVALID
+    assert fcache(L, out=None) == INVALID
+    assert fcache(L, lse=None) == INVALID
+    assert fcache(L, scale=-1.0) == INVALID
+
+
+def test_kv_cache_append_validation(L):
+    f = L.nc_kv_cache_append
+    assert f(BF16, 2, 8, 2, 64, 7, A, A, A, A, A, None) == INVALID  # T_max < Tq
+    assert f(BF16, 2, 8, 2, 64, 64, None, A, A, A, A, None) == INVALID
+    assert f(BF16, 2, 8, 2, 64, 64, A, A, A, A + 8, A, None) == INVALID
+    assert f(BF16, 2, 8, 2, 64, 64, A, A, A, A, None, None) == INVALID
+    assert f(BF16, 2, 8, 2, 64, 64, A, A, A, A, A + 2, None) == INVALID
+    assert f(BF16, 2, 0, 2, 64, 64, A, A, A, A, A, None) == INVALID
+    assert f(BF16, 2, 8, 2, 40, 64, A, A, A, A, A, None) == UNSUPPORTED

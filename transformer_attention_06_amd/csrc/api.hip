@@ -143,9 +143,53 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
   NC_TRY(check_ptr(lse, "lse"));
   NC_TRY(check_scale(scale));
   NC_TRY(check_device(nullptr));
-  nc::FwdParams p{q, k, v, out, lse, B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f};
+  nc::FwdParams p{q, k, v, out, lse, B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f,
+                  nullptr, T};
   hipStream_t s = (hipStream_t)stream;
   return finish(dt == NC_BF16 ? nc::launch_attn_fwd_bf16(p, s) : nc::launch_attn_fwd_f32(p, s), s, "nc_attn_fwd");
+}
+
+nc_status nc_attn_fwd_cache(nc_dtype dt, int B, int Tq, int H, int Hkv, int D, int T_max, const void* q,
+                            const void* k_cache, const void* v_cache, const int32_t* cache_seqlens, int window,
+                            float scale, void* out, float* lse, nc_stream stream) {
+  NC_TRY(check_shape(dt, B, Tq, H, Hkv, D));
+  if (T_max < Tq) return fail(NC_ERR_INVALID_ARG, "T_max=%d is smaller than the chunk Tq=%d", T_max, Tq);
+  if ((long long)B * T_max * Hkv * D > kMaxElems)
+    return fail(NC_ERR_UNSUPPORTED, "cache of B*T_max*Hkv*D elements exceeds 2^31-1");
+  NC_TRY(check_ptr(q, "q"));
+  NC_TRY(check_ptr(k_cache, "k_cache"));
+  NC_TRY(check_ptr(v_cache, "v_cache"));
+  if (!cache_seqlens) return fail(NC_ERR_INVALID_ARG, "cache_seqlens is NULL");
+  if (((uintptr_t)cache_seqlens & 3u) != 0) return fail(NC_ERR_INVALID_ARG, "cache_seqlens is not 4-byte aligned");
+  NC_TRY(check_ptr(out, "out"));
+  NC_TRY(check_ptr(lse, "lse"));
+  NC_TRY(check_scale(scale));
+  NC_TRY(check_device(nullptr));
+  nc::FwdParams p{q, k_cache, v_cache, out, lse, B, Tq, H, Hkv, D, norm_window(window, T_max), scale,
+                  scale * 1.4426950408889634f, cache_seqlens, T_max};
+  hipStream_t s = (hipStream_t)stream;
+  return finish(dt == NC_BF16 ? nc::launch_attn_fwd_bf16(p, s) : nc::launch_attn_fwd_f32(p, s), s,
+                "nc_attn_fwd_cache");
+}
+
+nc_status nc_kv_cache_append(nc_dtype dt, int B, int Tq, int Hkv, int D, int T_max, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache, const int32_t* cache_seqlens,
+                             nc_stream stream) {
+  NC_TRY(check_shape(dt, B, Tq, Hkv, Hkv, D));
+  if (T_max < Tq) return fail(NC_ERR_INVALID_ARG, "T_max=%d is smaller than the chunk Tq=%d", T_max, Tq);
+  if ((long long)B * T_max * Hkv * D > kMaxElems)
+    return fail(NC_ERR_UNSUPPORTED, "cache of B*T_max*Hkv*D elements exceeds 2^31-1");
+  NC_TRY(check_ptr(k_new, "k_new"));
+  NC_TRY(check_ptr(v_new, "v_new"));
+  NC_TRY(check_ptr(k_cache, "k_cache"));
+  NC_TRY(check_ptr(v_cache, "v_cache"));
+  if (!cache_seqlens) return fail(NC_ERR_INVALID_ARG, "cache_seqlens is NULL");
+  if (((uintptr_t)cache_seqlens & 3u) != 0) return fail(NC_ERR_INVALID_ARG, "cache_seqlens is not 4-byte aligned");
+  NC_TRY(check_device(nullptr));
+  hipStream_t s = (hipStream_t)stream;
+  return finish(nc::launch_cache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, B, Tq, Hkv, D, T_max,
+                                        dt == NC_BF16 ? 2 : 4, s),
+                s, "nc_kv_cache_append");
 }
 
 size_t nc_attn_bwd_workspace_bytes(nc_dtype dt, int B, int T, int H, int Hkv, int D) {

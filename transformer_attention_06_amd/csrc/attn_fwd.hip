@@ -23,6 +23,10 @@
 //     factor 2^8, so the O rescale is rare;
 //   * tiles entirely outside the causal band or window are never visited;
 //     element masks are applied only on tiles that cut the band's edges.
+// Both kernels also take a chunk of queries against a KV cache (the SDPA
+// fallback's chunked-inference case, "nanochat Admin & Developer Guide",
+// section 6): chunk row t of batch row b sits at position q_off[b] + t and
+// the band is shifted by q_off[b]; keys are read from the cache rows.
 // f32 kernel: plain per-query loop in float32, for the fp32 configurations.
 
 #include <math.h>
@@ -74,12 +78,29 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   const int grp = lane >> 4, t16 = lane & 15;
 
   const size_t qrs = (size_t)p.H * D;
+  // position of chunk row 0 (0 without a cache) and the keys present
+  const int off = p.q_off ? __builtin_amdgcn_readfirstlane(p.q_off[b]) : 0;
+  const int Tk = off + T;
+  if (off < 0 || Tk > p.T_kv) {  // a cache length the host could not check: NaN rows
+    const int qt_a = nqt - 1 - r_pair, qt_b = r_pair;
+    for (int pass = 0; pass < (paired && qt_b < qt_a ? 2 : 1); ++pass) {
+      const int q0 = (pass == 0 ? qt_a : qt_b) * FWD_BM;
+      for (int i = tid; i < FWD_BM * (D / 8); i += FWD_THREADS) {
+        const int r = q0 + i / (D / 8);
+        if (r < T)
+          *(u32x4*)((unsigned short*)p.out + ((size_t)b * T + r) * qrs + (size_t)h * D + (i % (D / 8)) * 8) =
+              (u32x4){0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+      }
+      if (tid < FWD_BM && q0 + tid < T) p.lse[((size_t)b * p.H + h) * T + q0 + tid] = NAN;
+    }
+    return;
+  }
   const unsigned kvrs = (unsigned)(p.Hkv * D);  // elements between consecutive positions
   const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
-  const unsigned short* kp = (const unsigned short*)p.k + (size_t)b * T * kvrs + (size_t)g * D;
-  const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * T * kvrs + (size_t)g * D;
-  // this (b, g)'s rows 0 .. T-1 span (T - 1) * kvrs + D elements
-  const unsigned span = (unsigned)(((size_t)(T - 1) * kvrs + D) * 2);
+  const unsigned short* kp = (const unsigned short*)p.k + (size_t)b * p.T_kv * kvrs + (size_t)g * D;
+  const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * p.T_kv * kvrs + (size_t)g * D;
+  // this (b, g)'s key rows 0 .. Tk-1 span (Tk - 1) * kvrs + D elements
+  const unsigned span = (unsigned)(((size_t)(Tk - 1) * kvrs + D) * 2);
   const BufDesc krs = buf_desc(kp, span), vrs = buf_desc(vp, span);
 
   const bool full = p.window <= 0;
@@ -88,16 +109,16 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   const unsigned wlim = full ? 0x80000000u : (unsigned)win;
   // key tiles [first, last] of query tile qt
   auto tile_range = [&](int qt, int& first, int& last) {
-    const int q0 = qt * FWD_BM;
+    const int q0 = off + qt * FWD_BM;  // position of the tile's first query
     first = (full ? 0 : max(0, q0 - win + 1)) / FWD_BN;
-    last = min(T - 1, q0 + FWD_BM - 1) / FWD_BN;
+    last = min(Tk - 1, q0 + FWD_BM - 1) / FWD_BN;
   };
 
   // Tile loads: lane l of instruction n writes tile row (inst*RPI + l/NC),
   // physical chunk l%NC, which holds logical chunk (l%NC) ^ swz(row). The
   // lane's source offset inside the tile is fixed; the tile and instruction
-  // offsets are uniform. The last tile may run past T: its rows are clamped
-  // to T-1 (finite data, masked for every valid query).
+  // offsets are uniform. The last tile may run past the keys present: its
+  // rows are clamped to Tk-1 (finite data, masked for every valid query).
   unsigned ld_off[IPW];
   int ld_row[IPW], ld_ch[IPW];
 #pragma unroll
@@ -109,7 +130,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   }
   auto issue_tile = [&](int jt, int buf) {
     const int j0 = jt * FWD_BN;
-    if (j0 + FWD_BN <= T) {
+    if (j0 + FWD_BN <= Tk) {
       const unsigned so = (unsigned)j0 * kvrs * 2u;
 #pragma unroll
       for (int n = 0; n < IPW; ++n) {
@@ -119,7 +140,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
     } else {
 #pragma unroll
       for (int n = 0; n < IPW; ++n) {
-        const int j = min(j0 + ld_row[n], T - 1);
+        const int j = min(j0 + ld_row[n], Tk - 1);
         const unsigned vo = (unsigned)(j * kvrs + ld_ch[n] * 8) * 2u;
         dma16(krs, vo, 0u, lds_u32(&kv_lds[buf][0][(wave * IPW + n) * RPI * D]));
         dma16(vrs, vo, 0u, lds_u32(&kv_lds[buf][1][(wave * IPW + n) * RPI * D]));
@@ -142,7 +163,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
   }
 
   // state of the query tile being processed
-  int qw = 0, qi = 0;    // first query of this wave, this lane's query
+  int qw = 0, qi = 0;    // positions of this wave's first query and of this lane's query
   bool q_valid = false;
   int t_end = 0;         // its last key tile
   int next_first = -1;   // first key tile of the next query tile (-1: none)
@@ -245,13 +266,14 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
 
   auto run = [&](int qt, int t_begin, auto startc) __attribute__((always_inline)) {
     constexpr int S0 = decltype(startc)::value;  // buffer of the first key tile
-    qw = qt * FWD_BM + wave * 32;
+    const int qrow = qt * FWD_BM + wave * 32 + li;  // this lane's query row of q / out
+    qw = off + qt * FWD_BM + wave * 32;
     qi = qw + li;
-    q_valid = qi < T;
+    q_valid = qrow < T;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       u32x4 w = {0u, 0u, 0u, 0u};
-      if (q_valid) w = *(const u32x4*)(qp + (size_t)qi * qrs + 16 * s + 8 * hh);
+      if (q_valid) w = *(const u32x4*)(qp + (size_t)qrow * qrs + 16 * s + 8 * hh);
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
     m2 = -INFINITY;
@@ -266,7 +288,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
     const float lt = sum_mod<32>(lsum);
     if (q_valid) {
       const float inv = 1.f / lt;
-      unsigned short* op = (unsigned short*)p.out + ((size_t)b * T + qi) * qrs + (size_t)h * D;
+      unsigned short* op = (unsigned short*)p.out + ((size_t)b * T + qrow) * qrs + (size_t)h * D;
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
@@ -276,7 +298,7 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
           w[1] = pk_bf16(o[d][4 * rg + 2] * inv, o[d][4 * rg + 3] * inv);
           *(u32x2*)(op + 32 * d + 8 * rg + 4 * hh) = w;
         }
-      if (hh == 0) p.lse[((size_t)b * p.H + h) * T + qi] = (m2 + __builtin_log2f(lt)) * kLn2;
+      if (hh == 0) p.lse[((size_t)b * p.H + h) * T + qrow] = (m2 + __builtin_log2f(lt)) * kLn2;
     }
   };
 
@@ -308,13 +330,21 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
 template <int D>
 __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(FwdParams p) {
   const int T = p.T;
-  const int qi = blockIdx.x * 64 + threadIdx.x;
+  const int qr_ = blockIdx.x * 64 + threadIdx.x;  // query row of q / out
   const int h = blockIdx.y, b = blockIdx.z;
-  if (qi >= T) return;
+  if (qr_ >= T) return;
+  const int off = p.q_off ? p.q_off[b] : 0;
+  float* o = (float*)p.out + (((size_t)b * T + qr_) * p.H + h) * D;
+  if (off < 0 || off + T > p.T_kv) {  // a cache length the host could not check: NaN row
+    for (int d = 0; d < D; ++d) o[d] = NAN;
+    p.lse[((size_t)b * p.H + h) * T + qr_] = NAN;
+    return;
+  }
+  const int qi = off + qr_;  // position
   const int g = h / (p.H / p.Hkv);
-  const float* q = (const float*)p.q + (((size_t)b * T + qi) * p.H + h) * D;
-  const float* kb = (const float*)p.k + ((size_t)b * T * p.Hkv + g) * D;
-  const float* vb = (const float*)p.v + ((size_t)b * T * p.Hkv + g) * D;
+  const float* q = (const float*)p.q + (((size_t)b * T + qr_) * p.H + h) * D;
+  const float* kb = (const float*)p.k + ((size_t)b * p.T_kv * p.Hkv + g) * D;
+  const float* vb = (const float*)p.v + ((size_t)b * p.T_kv * p.Hkv + g) * D;
   const size_t rs = (size_t)p.Hkv * D;
   float qr[D], acc[D];
 #pragma unroll
@@ -339,11 +369,10 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(FwdParams p) {
     for (int d = 0; d < D; ++d) acc[d] = fmaf(acc[d], a, e * vr[d]);
     m = mn;
   }
-  float* o = (float*)p.out + (((size_t)b * T + qi) * p.H + h) * D;
   const float inv = 1.f / l;
 #pragma unroll
   for (int d = 0; d < D; ++d) o[d] = acc[d] * inv;
-  p.lse[((size_t)b * p.H + h) * T + qi] = m + logf(l);
+  p.lse[((size_t)b * p.H + h) * T + qr_] = m + logf(l);
 }
 
 }  // namespace

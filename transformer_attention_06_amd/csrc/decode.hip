@@ -21,6 +21,8 @@
 //   1..T_max yields NaN out and lse for that row.
 // replicate: copies a batch-1 prompt cache row into every decode row (section
 //   7: the prompt is prefilled once and its cache copied to the samples).
+// cache_append: writes a chunk's k and v into the cache slots that follow
+//   each row's cached tokens (the in-place update of section 7, for a chunk).
 
 #include <math.h>
 
@@ -250,7 +252,36 @@ __global__ __launch_bounds__(256) void replicate_kernel(const u32x4* __restrict_
   }
 }
 
+// Chunk append: 16-byte vectors of k_new / v_new [B, Tq, Hkv, D] into cache
+// slots n_b .. n_b + Tq - 1; rows whose slots do not fit write nothing.
+__global__ __launch_bounds__(256) void cache_append_kernel(const u32x4* __restrict__ kn, const u32x4* __restrict__ vn,
+                                                           u32x4* __restrict__ kc, u32x4* __restrict__ vc,
+                                                           const int32_t* __restrict__ lens, int B, int Tq,
+                                                           int T_max, size_t vec_per_pos) {
+  const size_t per_row = (size_t)Tq * vec_per_pos, total = per_row * B;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += (size_t)gridDim.x * blockDim.x) {
+    const int b = (int)(i / per_row);
+    const size_t r = i - (size_t)b * per_row;
+    const int n = lens[b];
+    if (n < 0 || n > T_max - Tq) continue;
+    const size_t dst = ((size_t)b * T_max + n) * vec_per_pos + r;
+    kc[dst] = kn[i];
+    vc[dst] = vn[i];
+  }
+}
+
 }  // namespace
+
+hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const int32_t* cache_seqlens, int B, int Tq, int Hkv, int D, int T_max,
+                               size_t elem_bytes, hipStream_t s) {
+  const size_t vec_per_pos = (size_t)Hkv * D * elem_bytes / 16;
+  const size_t total = vec_per_pos * Tq * B;
+  const unsigned blocks = (unsigned)std::min<size_t>((total + 255) / 256, 8192);
+  cache_append_kernel<<<blocks, 256, 0, s>>>((const u32x4*)k_new, (const u32x4*)v_new, (u32x4*)k_cache,
+                                             (u32x4*)v_cache, cache_seqlens, B, Tq, T_max, vec_per_pos);
+  return hipGetLastError();
+}
 
 hipError_t launch_replicate(const void* src, void* dst, size_t n_bytes, int n_rows, size_t row_stride, hipStream_t s) {
   const size_t nvec = n_bytes / 16;

@@ -17,6 +17,12 @@ struct FwdParams {
   int window;        // 0 = full causal, otherwise 1 <= window < T
   float scale;       // logit scale
   float scale_log2;  // scale * log2(e)
+  // Chunk against a cache (q_off != nullptr): q/out hold T chunk rows per
+  // batch row, k/v are caches of T_kv positions per batch row, and chunk row
+  // t of batch row b sits at position q_off[b] + t, seeing cache positions
+  // up to that one. Without it T_kv == T and positions are the rows.
+  const int32_t* q_off;
+  int T_kv;
 };
 
 struct BwdParams {
@@ -111,6 +117,11 @@ hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s, const BwdEven
 hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s, const BwdEvents& ev);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t s);
 hipError_t launch_decode_append(const AppendParams& p, bool bf16, hipStream_t s);
+// Chunk k/v [B, Tq, Hkv, D] into cache slots cache_seqlens[b] .. + Tq - 1 (rows
+// whose slots do not fit are left alone).
+hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               const int32_t* cache_seqlens, int B, int Tq, int Hkv, int D, int T_max,
+                               size_t elem_bytes, hipStream_t s);
 // Copies the first n_bytes of src into n_rows rows of dst spaced row_stride bytes apart.
 hipError_t launch_replicate(const void* src, void* dst, size_t n_bytes, int n_rows, size_t row_stride, hipStream_t s);
 hipError_t launch_rope_table(int T_rope, int D, double base, float* c, float* sn, hipStream_t s);

@@ -22,7 +22,7 @@ STATUS = {0: "NC_OK", 1: "NC_ERR_INVALID_ARG", 2: "NC_ERR_UNSUPPORTED", 3: "NC_E
 # every symbol include/ncattn.h declares
 EXPORTS = (
     "nc_abi_version", "nc_status_string", "nc_last_error_message",
-    "nc_attn_fwd", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd", "nc_attn_bwd_prologue",
+    "nc_attn_fwd", "nc_attn_fwd_cache", "nc_kv_cache_append", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd", "nc_attn_bwd_prologue",
     "nc_profile_bwd_main",
     "nc_attn_decode_workspace_bytes", "nc_attn_decode",
     "nc_attn_decode_step_workspace_bytes", "nc_attn_decode_step", "nc_kv_cache_replicate",
@@ -46,6 +46,8 @@ _SIGS = {
     "nc_status_string": ([_i], ctypes.c_char_p),
     "nc_last_error_message": ([], ctypes.c_char_p),
     "nc_attn_fwd": ([_i] * 6 + [_p, _p, _p, _i, _f, _p, _p, _p], _i),
+    "nc_attn_fwd_cache": ([_i] * 7 + [_p] * 4 + [_i, _f, _p, _p, _p], _i),
+    "nc_kv_cache_append": ([_i] * 6 + [_p] * 5 + [_p], _i),
     "nc_attn_bwd_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_bwd": ([_i] * 6 + [_p] * 6 + [_i, _f] + [_p] * 3 + [_p, _sz, _p], _i),
     "nc_attn_bwd_prologue": ([_i] * 6 + [_p] * 6 + [_i, _f] + [_p] * 5 + [_i, _f] + [_p] * 3
@@ -185,6 +187,36 @@ def nc_profile_bwd_main(dq_begin=None, dkdv_begin=None, end=None):
     with no arguments to stop."""
     evs = [e.cuda_event if e is not None else None for e in (dq_begin, dkdv_begin, end)]
     _raise_on("nc_profile_bwd_main", lib().nc_profile_bwd_main(*evs))
+
+
+def nc_attn_fwd_cache(q, k_cache, v_cache, cache_seqlens, window, scale, out=None, lse=None, stream=None):
+    """A chunk q [B,Tq,H,D] against caches [B,T_max,Hkv,D] already holding the chunk's keys at
+    slots cache_seqlens[b] .. + Tq - 1 -> (out [B,Tq,H,D], lse [B,H,Tq] float32)."""
+    import torch
+    B, Tq, H, D = q.shape
+    T_max, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if cache_seqlens.dtype != torch.int32:
+        raise TypeError("cache_seqlens must be int32")
+    out = _empty(q.shape, q) if out is None else out
+    lse = _empty((B, H, Tq), q, torch.float32) if lse is None else lse
+    st = lib().nc_attn_fwd_cache(_dt(q), B, Tq, H, Hkv, D, T_max, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                 _ptr(cache_seqlens), int(window), float(scale), _ptr(out), _ptr(lse),
+                                 _stream(stream))
+    _raise_on("nc_attn_fwd_cache", st)
+    return out, lse
+
+
+def nc_kv_cache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, stream=None):
+    """Writes k_new/v_new [B,Tq,Hkv,D] into cache slots cache_seqlens[b] .. + Tq - 1 (in place)."""
+    import torch
+    B, Tq, Hkv, D = k_new.shape
+    T_max = k_cache.shape[1]
+    if cache_seqlens.dtype != torch.int32:
+        raise TypeError("cache_seqlens must be int32")
+    st = lib().nc_kv_cache_append(_dt(k_new), B, Tq, Hkv, D, T_max, _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                                  _ptr(v_cache), _ptr(cache_seqlens), _stream(stream))
+    _raise_on("nc_kv_cache_append", st)
+    return k_cache, v_cache
 
 
 def nc_attn_decode_workspace_bytes(dtype_code, B, H, Hkv, D, T_max):
