@@ -100,7 +100,7 @@ def main():
     import torch
 
     from transformer_attention_06_amd import native, synth
-    from transformer_attention_06_amd.workload import (FULL, attn_flops, band_pairs, decode_bytes,
+    from transformer_attention_06_amd.workload import (FULL, attn_flops, band_pairs, chunk_pairs, decode_bytes,
                                                        decode_step_bytes, workloads)
 
     if not torch.cuda.is_available():
@@ -272,7 +272,39 @@ def main():
             "ms_per_step": round(sms, 4), "bytes_per_step": sbytes, "gbs": round(sgbs, 1),
             "frac_hbm_peak": round(sgbs / PEAK_HBM_GBS, 4)}
         log("decode step:", json.dumps(decode["step_with_append"]))
-        del kc, vc
+
+        # chunked prefill against the same caches: a 512-token chunk per row at
+        # seeded offsets uniform on 0 .. T_max - 512 (its keys taken as already
+        # appended), 20 layers with the SSSL windows
+        CQ = 512
+        coff = np.random.default_rng(2006).integers(0, Tm - CQ + 1, DB).astype(np.int32)
+        coff_d = torch.from_numpy(coff).to(dev)
+        cq_ = [synth.normal_device((DB, CQ, DH, DD), 2007 + 10 * l, "bf16") for l in range(len(dw.windows))]
+        cout = torch.empty_like(cq_[0])
+        clse = torch.empty((DB, DH, CQ), dtype=torch.float32, device=dev)
+
+        def cstep():
+            for l, w in enumerate(dw.windows):
+                native.nc_attn_fwd_cache(cq_[l], kc[l], vc[l], coff_d, w, dw.scale, out=cout, lse=clse)
+
+        for _ in range(args.warmup):
+            cstep()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            cstep()
+        t1.record()
+        torch.cuda.synchronize()
+        cms = t0.elapsed_time(t1) / args.steps
+        cflops = sum(4 * DD * DH * chunk_pairs(int(n0), CQ, w) for w in dw.windows for n0 in coff)
+        ctf = cflops / (cms * 1e-3) / 1e12
+        decode["prefill_chunk"] = {
+            "what": "nc_attn_fwd_cache per layer: 64 rows x 512-token chunk at offsets uniform 0..1536 "
+                    "against the [64, 2048, 10, 128] caches, 20-layer SSSL windows",
+            "ms_per_step": round(cms, 4), "band_flops": cflops, "tflops": round(ctf, 2),
+            "frac_bf16_peak": round(ctf / PEAK_BF16_TFLOPS, 4)}
+        log("prefill chunk:", json.dumps(decode["prefill_chunk"]))
+        del kc, vc, cq_
 
     # ------------------------------------------------------------- roofline
     dom = max(("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"), key=lambda k: kern[k]["ms_per_step"])

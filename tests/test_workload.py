@@ -74,3 +74,13 @@ def test_decode_step_bytes_brute_force():
             total += len(old) * Hkv * D * 2 * 2 + Hkv * D * 2 * 2 + (H + 2 * Hkv) * D * 2
             total += H * D * 2 + H * 4 + 4 + D * 4
         assert W.decode_step_bytes(n_cached, H, Hkv, D, w) == total
+
+
+def test_chunk_pairs_brute_force():
+    for n in (0, 1, 5, 40, 300):
+        for Tq in (1, 2, 17, 64):
+            for w in (0, 1, 3, 6, 41, 100, 400):
+                want = sum(min(n + t + 1, w) if w > 0 else n + t + 1 for t in range(Tq))
+                assert W.chunk_pairs(n, Tq, w) == want, (n, Tq, w)
+    assert W.chunk_pairs(0, 2048, 0) == W.band_pairs(2048, 0)
+    assert W.chunk_pairs(0, 2048, 1024) == W.band_pairs(2048, 1024)

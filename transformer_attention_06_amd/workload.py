@@ -53,6 +53,19 @@ def attn_flops(B, T, H, D, windows, kind="fwd"):
     return sum(B * H * band_pairs(T, w) * per_pair for w in windows)
 
 
+def chunk_pairs(n_cached, Tq, window):
+    """Visible (query, key) pairs of one (b, h) for a chunk of Tq queries after
+    n_cached cached tokens: query t at position p = n_cached + t sees
+    min(p + 1, window) keys (p + 1 for a full layer)."""
+    lo, hi = n_cached + 1, n_cached + Tq  # keys seen by the first and last query, full layer
+    if window <= 0 or window >= hi:
+        return (lo + hi) * Tq // 2
+    if window <= lo:
+        return window * Tq
+    ramp = window - lo  # queries still below the window
+    return (lo + window - 1) * ramp // 2 + window * (Tq - ramp)
+
+
 def decode_keys(seqlen, window):
     """Keys a decode query at length seqlen reads."""
     return seqlen if is_full(window, seqlen) else window
