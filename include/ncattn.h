@@ -100,7 +100,9 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
  *   s_tj = scale * <q[b,t,h], k_cache[b,j,g]>.
  * Same kernels and numerics as nc_attn_fwd (which is this call with n = 0,
  * Tq = T_max = T). cache_seqlens is a DEVICE int32 array [B]; a row with
- * n < 0 or n + Tq > T_max gets NaN out and lse.
+ * n < 0 or n + Tq > T_max gets NaN out and lse. Keys are read in tiles of 64
+ * positions and masked, so slots 0 .. n + Tq - 1 must hold finite values
+ * (as they do once earlier steps have filled them); later slots are not read.
  *   q [B,Tq,H,D] (after the prologue, e.g. nc_qk_prologue_fwd with
  *   pos_offset = cache_seqlens), k_cache/v_cache [B,T_max,Hkv,D]
  *   -> out [B,Tq,H,D], lse [B,H,Tq]
