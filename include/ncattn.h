@@ -276,6 +276,34 @@ nc_status nc_qk_prologue_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
                              float eps, void* q_out, void* k_out, nc_stream stream);
 
 /*
+ * QK prologue and attention forward in one call: the result of
+ * nc_qk_prologue_fwd (q_out = q', k_out = k') followed by nc_attn_fwd on q',
+ * k', v ("nanochat Admin & Developer Guide", section 3: q and k are
+ * RMS-normalised and rotated right before attention). For bf16 the keys go
+ * through the prologue kernel alone and the forward kernel applies the
+ * prologue to each query row as it loads it, storing q' (the backward needs
+ * q' and k'); q' and k' are the bf16 values the attention uses. The row sums
+ * of squares are added in a different order than the prologue kernel's, so
+ * q_out may differ from nc_qk_prologue_fwd's by one bf16 rounding in rare
+ * elements. Arguments as for nc_qk_prologue_fwd and nc_attn_fwd; outputs
+ * must not alias inputs.
+ */
+nc_status nc_attn_fwd_prologue(nc_dtype dt, int B, int T, int H, int Hkv, int D,
+                               const void* q_raw, const void* k_raw, const void* v,
+                               const int32_t* pos_offset, const float* cos_tab,
+                               const float* sin_tab, int T_rope, float eps,
+                               int window, float scale, void* q_out, void* k_out,
+                               void* out, float* lse, nc_stream stream);
+
+/*
+ * Measurement aid, like nc_profile_bwd_main: while set on the calling thread,
+ * every nc_attn_fwd_prologue call records prologue_begin before its prologue
+ * kernel, fwd_begin between it and the forward kernel, and end after that.
+ * All three hipEvent_t or none (NULL clears); NC_ERR_INVALID_ARG otherwise.
+ */
+nc_status nc_profile_fwd_prologue(void* prologue_begin, void* fwd_begin, void* end);
+
+/*
  * QK prologue backward: given dq_out, dk_out (gradients w.r.t. the prologue
  * outputs) and the raw q, k, writes dq, dk w.r.t. the raw inputs:
  *   u = R(-theta) dy,  r = sqrt(mean x^2 + eps),  dx = u / r - x <x, u> / (D r^3).

@@ -273,3 +273,25 @@ def test_kv_cache_append_validation(L):
     assert f(BF16, 2, 8, 2, 64, 64, A, A, A, A, A + 2, None) == INVALID
     assert f(BF16, 2, 0, 2, 64, 64, A, A, A, A, A, None) == INVALID
     assert f(BF16, 2, 8, 2, 40, 64, A, A, A, A, A, None) == UNSUPPORTED
+
+
+def test_fwd_prologue_validation(L):
+    f = L.nc_attn_fwd_prologue
+
+    def call(q=A, k=A, v=A, pos=None, T=64, T_rope=128, eps=1e-6, qo=A, ko=A, out=A, lse=A, D=64, scale=0.1):
+        return f(BF16, 1, T, 2, 1, D, q, k, v, pos, A, A, T_rope, eps, 0, scale, qo, ko, out, lse, None)
+
+    assert call(q=None) == INVALID
+    assert call(v=None) == INVALID
+    assert call(T_rope=32) == INVALID
+    assert "table" in msg(L)
+    assert call(pos=A + 2) == INVALID
+    assert call(eps=-1.0) == INVALID
+    assert call(qo=None) == INVALID
+    assert call(ko=A + 4) == INVALID
+    assert call(out=None) == INVALID
+    assert call(lse=None) == INVALID
+    assert call(scale=float("inf")) == INVALID
+    assert call(D=80) == UNSUPPORTED
+    assert L.nc_profile_fwd_prologue(A, None, A) == INVALID
+    assert L.nc_profile_fwd_prologue(None, None, None) == OK

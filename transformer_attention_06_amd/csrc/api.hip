@@ -22,6 +22,7 @@ namespace {
 
 thread_local char g_msg[512] = "";
 thread_local nc::BwdEvents g_bwd_ev = {nullptr, nullptr, nullptr};
+thread_local hipEvent_t g_fwd_ev[3] = {nullptr, nullptr, nullptr};  // k prologue, forward, end
 
 nc_status fail(nc_status s, const char* fmt, ...) {
   va_list ap;
@@ -144,7 +145,7 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
   NC_TRY(check_scale(scale));
   NC_TRY(check_device(nullptr));
   nc::FwdParams p{q, k, v, out, lse, B, T, H, Hkv, D, norm_window(window, T), scale, scale * 1.4426950408889634f,
-                  nullptr, T};
+                  nullptr, T, nullptr, nullptr, nullptr, nullptr, 0, 0.f};
   hipStream_t s = (hipStream_t)stream;
   return finish(dt == NC_BF16 ? nc::launch_attn_fwd_bf16(p, s) : nc::launch_attn_fwd_f32(p, s), s, "nc_attn_fwd");
 }
@@ -166,7 +167,7 @@ nc_status nc_attn_fwd_cache(nc_dtype dt, int B, int Tq, int H, int Hkv, int D, i
   NC_TRY(check_scale(scale));
   NC_TRY(check_device(nullptr));
   nc::FwdParams p{q, k_cache, v_cache, out, lse, B, Tq, H, Hkv, D, norm_window(window, T_max), scale,
-                  scale * 1.4426950408889634f, cache_seqlens, T_max};
+                  scale * 1.4426950408889634f, cache_seqlens, T_max, nullptr, nullptr, nullptr, nullptr, 0, 0.f};
   hipStream_t s = (hipStream_t)stream;
   return finish(dt == NC_BF16 ? nc::launch_attn_fwd_bf16(p, s) : nc::launch_attn_fwd_f32(p, s), s,
                 "nc_attn_fwd_cache");
@@ -410,6 +411,49 @@ static nc_status prologue_common(nc_dtype dt, int B, int T, int H, int Hkv, int 
   if (T_rope < 1) return fail(NC_ERR_INVALID_ARG, "T_rope must be >= 1");
   if (!pos_offset && T > T_rope) return fail(NC_ERR_INVALID_ARG, "T=%d exceeds the table length %d", T, T_rope);
   if (!(eps >= 0.f) || !isfinite(eps)) return fail(NC_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return NC_OK;
+}
+
+nc_status nc_attn_fwd_prologue(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q_raw,
+                               const void* k_raw, const void* v, const int32_t* pos_offset, const float* cos_tab,
+                               const float* sin_tab, int T_rope, float eps, int window, float scale, void* q_out,
+                               void* k_out, void* out, float* lse, nc_stream stream) {
+  NC_TRY(prologue_common(dt, B, T, H, Hkv, D, q_raw, k_raw, pos_offset, cos_tab, sin_tab, T_rope, eps));
+  NC_TRY(check_ptr(v, "v"));
+  NC_TRY(check_ptr(q_out, "q_out"));
+  NC_TRY(check_ptr(k_out, "k_out"));
+  NC_TRY(check_ptr(out, "out"));
+  NC_TRY(check_ptr(lse, "lse"));
+  NC_TRY(check_scale(scale));
+  NC_TRY(check_device(nullptr));
+  hipStream_t s = (hipStream_t)stream;
+  const bool bf16 = dt == NC_BF16;
+  // bf16: the keys' prologue alone (no query rows), then the forward applies
+  // the queries' prologue as it loads them. float32: both prologues, then the
+  // plain forward on their outputs.
+  nc::PrologueParams pp{q_raw, k_raw, pos_offset, cos_tab, sin_tab, nullptr, nullptr, q_out, k_out,
+                        B, T, bf16 ? 0 : H, Hkv, D, T_rope, eps};
+  hipError_t e = hipSuccess;
+  if (g_fwd_ev[0]) e = hipEventRecord(g_fwd_ev[0], s);
+  if (e == hipSuccess) e = nc::launch_prologue(pp, bf16, false, s);
+  if (e == hipSuccess && g_fwd_ev[1]) e = hipEventRecord(g_fwd_ev[1], s);
+  if (e == hipSuccess) {
+    nc::FwdParams p{bf16 ? q_raw : q_out, k_out, v, out, lse, B, T, H, Hkv, D, norm_window(window, T), scale,
+                    scale * 1.4426950408889634f, nullptr, T, bf16 ? q_out : nullptr, pos_offset, cos_tab, sin_tab,
+                    T_rope, eps};
+    e = bf16 ? nc::launch_attn_fwd_bf16(p, s) : nc::launch_attn_fwd_f32(p, s);
+  }
+  if (e == hipSuccess && g_fwd_ev[2]) e = hipEventRecord(g_fwd_ev[2], s);
+  return finish(e, s, "nc_attn_fwd_prologue");
+}
+
+nc_status nc_profile_fwd_prologue(void* prologue_begin, void* fwd_begin, void* end) {
+  const int set = (prologue_begin != nullptr) + (fwd_begin != nullptr) + (end != nullptr);
+  if (set != 0 && set != 3) return fail(NC_ERR_INVALID_ARG, "the three events must all be set or all be NULL");
+  g_fwd_ev[0] = (hipEvent_t)prologue_begin;
+  g_fwd_ev[1] = (hipEvent_t)fwd_begin;
+  g_fwd_ev[2] = (hipEvent_t)end;
+  g_msg[0] = 0;
   return NC_OK;
 }
 

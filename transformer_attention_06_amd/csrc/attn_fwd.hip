@@ -27,6 +27,9 @@
 // fallback's chunked-inference case, "nanochat Admin & Developer Guide",
 // section 6): chunk row t of batch row b sits at position q_off[b] + t and
 // the band is shifted by q_off[b]; keys are read from the cache rows.
+// The bf16 kernel can also take raw queries and apply the QK prologue to each
+// row as it loads it (section 3: weightless RMSNorm, then half-split RoPE),
+// storing q' for the backward; the keys then come from a k-only prologue.
 // f32 kernel: plain per-query loop in float32, for the fp32 configurations.
 
 #include <math.h>
@@ -43,7 +46,7 @@ constexpr int FWD_BM = 128;  // queries per workgroup
 constexpr int FWD_BN = 64;   // keys per tile
 constexpr int FWD_THREADS = 256;
 
-template <int D>
+template <int D, bool PRO>
 __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams p) {
   constexpr int NC = D / 8;  // 16-byte chunks per row (LDS tiles are swizzled, unpadded)
   constexpr int NS = D / 16;
@@ -96,6 +99,8 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
     return;
   }
   const unsigned kvrs = (unsigned)(p.Hkv * D);  // elements between consecutive positions
+  // RoPE position of query row 0 (query prologue only)
+  const int pos0 = PRO && p.pos_offset ? __builtin_amdgcn_readfirstlane(p.pos_offset[b]) : 0;
   const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
   const unsigned short* kp = (const unsigned short*)p.k + (size_t)b * p.T_kv * kvrs + (size_t)g * D;
   const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * p.T_kv * kvrs + (size_t)g * D;
@@ -276,6 +281,60 @@ __global__ __launch_bounds__(FWD_THREADS, 2) void attn_fwd_bf16_kernel(FwdParams
       if (q_valid) w = *(const u32x4*)(qp + (size_t)qrow * qrs + 16 * s + 8 * hh);
       qf[s] = __builtin_bit_cast(bf16x8, w);
     }
+    // query prologue: the lane's cos/sin rows are requested right after q
+    const int pos = qrow + pos0;
+    const bool pos_ok = pos >= 0 && pos < p.T_rope;
+    f32x4 cv[PRO ? NS / 2 : 1][2], sv[PRO ? NS / 2 : 1][2];
+    if constexpr (PRO) {
+      const size_t toff = (size_t)((q_valid && pos_ok) ? pos : 0) * (D / 2) + 8 * hh;
+#pragma unroll
+      for (int s = 0; s < NS / 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          cv[s][i] = *(const f32x4*)(p.cos_tab + toff + 16 * s + 4 * i);
+          sv[s][i] = *(const f32x4*)(p.sin_tab + toff + 16 * s + 4 * i);
+        }
+    }
+    if constexpr (PRO) {
+      // RMSNorm + RoPE of this lane's query row in the operand layout: the lane
+      // holds elements 16 s + 8 hh + e, and element d < D/2 pairs with
+      // d + D/2, held by the same lane at s + NS/2. The sum of squares adds
+      // the two half-waves' shares, taken straight from the packed row. q' is
+      // rounded to bf16, used and stored.
+      float ss = 0.f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const u32x4 w = __builtin_bit_cast(u32x4, qf[s]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = __builtin_bit_cast(float, w[i] << 16), hi = __builtin_bit_cast(float, w[i] & 0xffff0000u);
+          ss = fmaf(lo, lo, fmaf(hi, hi, ss));
+        }
+      }
+      ss = sum_mod<32>(ss);
+      const float inv_r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+      unsigned short* qo = (unsigned short*)p.q_out + ((size_t)b * T + qrow) * qrs + (size_t)h * D;
+#pragma unroll
+      for (int s = 0; s < NS / 2; ++s) {
+        float xl[8], xh[8];
+        unpack8_bf16(__builtin_bit_cast(u32x4, qf[s]), xl);
+        unpack8_bf16(__builtin_bit_cast(u32x4, qf[s + NS / 2]), xh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float cs = cv[s][e >> 2][e & 3], sn = sv[s][e >> 2][e & 3];
+          const float a = xl[e] * inv_r, bb = xh[e] * inv_r;
+          xl[e] = pos_ok ? fmaf(a, cs, -bb * sn) : NAN;
+          xh[e] = pos_ok ? fmaf(a, sn, bb * cs) : NAN;
+        }
+        const u32x4 wl = pack8_bf16(xl), wh = pack8_bf16(xh);
+        qf[s] = __builtin_bit_cast(bf16x8, wl);
+        qf[s + NS / 2] = __builtin_bit_cast(bf16x8, wh);
+        if (q_valid) {
+          *(u32x4*)(qo + 16 * s + 8 * hh) = wl;
+          *(u32x4*)(qo + 16 * (s + NS / 2) + 8 * hh) = wh;
+        }
+      }
+    }
     m2 = -INFINITY;
     lsum = 0.f;
 #pragma unroll
@@ -375,18 +434,24 @@ __global__ __launch_bounds__(64) void attn_fwd_f32_kernel(FwdParams p) {
   p.lse[((size_t)b * p.H + h) * T + qr_] = m + logf(l);
 }
 
-}  // namespace
 
-hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s) {
+template <bool PRO>
+hipError_t launch_fwd_bf16(const FwdParams& p, hipStream_t s) {
   const int nqt = (p.T + FWD_BM - 1) / FWD_BM;
   const dim3 grid((p.window <= 0 ? (nqt + 1) / 2 : nqt) * p.H * p.B), block(FWD_THREADS);
   switch (p.D) {
-    case 32: attn_fwd_bf16_kernel<32><<<grid, block, 0, s>>>(p); break;
-    case 64: attn_fwd_bf16_kernel<64><<<grid, block, 0, s>>>(p); break;
-    case 128: attn_fwd_bf16_kernel<128><<<grid, block, 0, s>>>(p); break;
+    case 32: attn_fwd_bf16_kernel<32, PRO><<<grid, block, 0, s>>>(p); break;
+    case 64: attn_fwd_bf16_kernel<64, PRO><<<grid, block, 0, s>>>(p); break;
+    case 128: attn_fwd_bf16_kernel<128, PRO><<<grid, block, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s) {
+  return p.q_out ? launch_fwd_bf16<true>(p, s) : launch_fwd_bf16<false>(p, s);
 }
 
 hipError_t launch_attn_fwd_f32(const FwdParams& p, hipStream_t s) {

@@ -23,6 +23,15 @@ struct FwdParams {
   // up to that one. Without it T_kv == T and positions are the rows.
   const int32_t* q_off;
   int T_kv;
+  // Query prologue in the forward (q_out != nullptr, bf16, no cache): q holds
+  // the raw queries; each row gets RMSNorm + RoPE at position
+  // (pos_offset ? pos_offset[b] : 0) + t as it is loaded, and q' goes to q_out.
+  void* q_out;
+  const int32_t* pos_offset;
+  const float* cos_tab;  // [T_rope, D/2]
+  const float* sin_tab;
+  int T_rope;
+  float eps;
 };
 
 struct BwdParams {

@@ -26,7 +26,8 @@ EXPORTS = (
     "nc_profile_bwd_main",
     "nc_attn_decode_workspace_bytes", "nc_attn_decode",
     "nc_attn_decode_step_workspace_bytes", "nc_attn_decode_step", "nc_kv_cache_replicate",
-    "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd",
+    "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd", "nc_attn_fwd_prologue",
+    "nc_profile_fwd_prologue",
 )
 
 
@@ -53,6 +54,7 @@ _SIGS = {
     "nc_attn_bwd_prologue": ([_i] * 6 + [_p] * 6 + [_i, _f] + [_p] * 5 + [_i, _f] + [_p] * 3
                              + [_p, _sz, _p], _i),
     "nc_profile_bwd_main": ([_p, _p, _p], _i),
+    "nc_profile_fwd_prologue": ([_p, _p, _p], _i),
     "nc_attn_decode_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_decode": ([_i] * 6 + [_p] * 4 + [_i, _f, _p, _p, _p, _sz, _p], _i),
     "nc_attn_decode_step_workspace_bytes": ([_i] * 6, _sz),
@@ -60,6 +62,7 @@ _SIGS = {
     "nc_kv_cache_replicate": ([_i] * 6 + [_p, _p, _p], _i),
     "nc_rope_table": ([_i, _i, _d, _p, _p, _p], _i),
     "nc_qk_prologue_fwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p], _i),
+    "nc_attn_fwd_prologue": ([_i] * 6 + [_p] * 6 + [_i, _f, _i, _f] + [_p] * 4 + [_p], _i),
     "nc_qk_prologue_bwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p, _p, _p], _i),
 }
 
@@ -219,6 +222,13 @@ def nc_kv_cache_append(k_new, v_new, k_cache, v_cache, cache_seqlens, stream=Non
     return k_cache, v_cache
 
 
+def nc_profile_fwd_prologue(prologue_begin=None, fwd_begin=None, end=None):
+    """Record torch.cuda.Events around the two kernels of later nc_attn_fwd_prologue calls on this
+    thread; call with no arguments to stop."""
+    evs = [e.cuda_event if e is not None else None for e in (prologue_begin, fwd_begin, end)]
+    _raise_on("nc_profile_fwd_prologue", lib().nc_profile_fwd_prologue(*evs))
+
+
 def nc_attn_decode_workspace_bytes(dtype_code, B, H, Hkv, D, T_max):
     return lib().nc_attn_decode_workspace_bytes(dtype_code, B, H, Hkv, D, T_max)
 
@@ -305,6 +315,24 @@ def nc_qk_prologue_fwd(q, k, cos, sin, eps, pos_offset=None, q_out=None, k_out=N
                                   _ptr(k_out), _stream(stream))
     _raise_on("nc_qk_prologue_fwd", st)
     return q_out, k_out
+
+
+def nc_attn_fwd_prologue(q, k, v, cos, sin, eps, window, scale, pos_offset=None, q_out=None, k_out=None,
+                         out=None, lse=None, stream=None):
+    """Prologue + attention forward from raw q [B,T,H,D], k [B,T,Hkv,D] ->
+    (q', k', out [B,T,H,D], lse [B,H,T] float32)."""
+    import torch
+    B, T, H, D = q.shape
+    Hkv = k.shape[2]
+    q_out = _empty(q.shape, q) if q_out is None else q_out
+    k_out = _empty(k.shape, k) if k_out is None else k_out
+    out = _empty(q.shape, q) if out is None else out
+    lse = _empty((B, H, T), q, torch.float32) if lse is None else lse
+    st = lib().nc_attn_fwd_prologue(_dt(q), B, T, H, Hkv, D, _ptr(q), _ptr(k), _ptr(v), _ptr(pos_offset),
+                                    _ptr(cos), _ptr(sin), cos.shape[0], float(eps), int(window), float(scale),
+                                    _ptr(q_out), _ptr(k_out), _ptr(out), _ptr(lse), _stream(stream))
+    _raise_on("nc_attn_fwd_prologue", st)
+    return q_out, k_out, out, lse
 
 
 def nc_qk_prologue_bwd(q, k, cos, sin, eps, dq_out, dk_out, pos_offset=None, dq=None, dk=None,
