@@ -25,7 +25,7 @@
 //   dkdv: one workgroup per (b, kv head, 128-key tile); each of the 4 waves
 //         keeps 32 keys' K and V fragments in registers and accumulates dK^T
 //         and dV^T for them over every query head of the GQA group and every
-//         64-query tile that intersects the band. S = Q K^T and dP = dO V^T
+//         128-query tile that intersects the band. S = Q K^T and dP = dO V^T
 //         come out with one key column per lane, which is directly the
 //         B-operand layout of dV^T += dO^T P and dK^T += Q^T dS; dO^T and
 //         Q^T are LDS transpose reads. Q/dO tiles and the per-row
@@ -45,7 +45,7 @@ namespace nc {
 namespace {
 
 constexpr int BWD_BN = 128;  // keys per workgroup (32 per wave)
-constexpr int BWD_BM = 64;   // queries per step
+constexpr int BWD_BM = 128;  // queries per step
 constexpr int BWD_THREADS = 256;
 constexpr int NBUF = 2;  // q/dO tile buffers: loads run one step ahead
 constexpr int DQ_BM = 128;  // queries per dq workgroup (32 per wave)
@@ -296,17 +296,19 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
           dma16(orsr, vo, 0u, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
         }
       }
-      if (wave < 2) {  // per-row statistics: wave 0 lse2, wave 1 delta (rows past T clamped)
-        const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + h) * T;
-        const int i = min(i0 + lane, T - 1);
-        dma4(buf_desc(src, (unsigned)T * 4u), (unsigned)i * 4u, 0u, lds_u32(wave == 0 ? lse2_lds[buf] : dl_lds[buf]));
+      {  // per-row statistics: waves 0/2 lse2, waves 1/3 delta, 64 rows each (rows past T clamped)
+        const bool isl = (wave & 1) == 0;
+        const int r0 = (wave >> 1) * 64;
+        const float* src = (isl ? p.lse2 : p.delta) + ((size_t)b * p.H + h) * T;
+        const int i = min(i0 + r0 + lane, T - 1);
+        dma4(buf_desc(src, (unsigned)T * 4u), (unsigned)i * 4u, 0u, lds_u32((isl ? lse2_lds[buf] : dl_lds[buf]) + r0));
       }
     };
 
     // Copies run NBUF - 1 steps ahead. Vector memory operations complete in
     // issue order, so the wait at the top of a step lets exactly the copies of
     // the later steps already issued stay in flight.
-    const int dma_ops = 2 * QIPW + (wave < 2 ? 1 : 0);  // copies this wave issues per step
+    const int dma_ops = 2 * QIPW + 1;  // copies this wave issues per step
     auto step_fn = [&](int step, auto bufc) __attribute__((always_inline)) {
       constexpr int buf = decltype(bufc)::value;
       const int hq = step / n_it;
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
       const unsigned short* ql = q_lds[buf];
       const unsigned short* ol = do_lds[buf];
 #pragma unroll
-      for (int ib = 0; ib < 2; ++ib) {
+      for (int ib = 0; ib < BWD_BM / 32; ++ib) {
         // Every LDS operand of this 32-query half is requested before the
         // first product: q and dO rows (S, dP), the row statistics, and the
         // dO^T / Q^T transpose reads (dV, dK).
