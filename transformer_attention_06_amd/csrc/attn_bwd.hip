@@ -426,6 +426,319 @@ __global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams
 }
 
 // --------------------------------------------------------------------------
+// dK and dV with 16 keys per wave: one workgroup per (b, kv head, 64-key
+// tile), 4 waves, two workgroups per CU, 16x16x32 bf16 MFMA, 64-query steps.
+// The same products as the kernel above; halving each wave's keys halves its
+// stationary registers (K, V fragments and the dK, dV accumulators), so two
+// waves of independent workgroups share each SIMD and hide each other's LDS
+// and arithmetic latency. Layouts (lane l,
+// t = l % 16, g = l / 16): A operands hold A[t][8 g + e], B operands
+// B[8 g + e][t], results C[4 g + r][t].
+//   S = Q K^T per 16-query block: A = q rows (LDS), B = K^T (registers),
+//     result: one key column per lane, queries 4 g + r of the block;
+//   dV^T += dO^T P and dK^T += Q^T dS per 16-wide block of d over 32 queries:
+//     A = dO^T / Q^T from transpose reads of rows {4 g .. 4 g + 3} and
+//     {16 + 4 g .. 16 + 4 g + 3}, B = P / dS of the lane's key for exactly
+//     those queries (the two 16-query blocks of S), so the contraction index
+//     is paired identically on both operands.
+constexpr int K16_WAVES = 4;               // waves per workgroup (two workgroups per CU)
+constexpr int K16_BN = 16 * K16_WAVES;     // keys per workgroup
+constexpr int K16_BM = 64;                 // queries per step
+constexpr int BWD16_THREADS = 64 * K16_WAVES;
+
+// Stores one head-vector gradient held in the 16x16 result layout: lane
+// (t, g) holds gr[db][r] = dy[16 db + 4 g + r] / mul; the lanes with the same
+// t hold the rest. Prologue backward as in store_grad_row. All 64 lanes must
+// call it; xw holds x[16 db + 4 g .. + 3] (nullptr: no prologue).
+template <int D>
+__device__ __forceinline__ void store_grad_row16(const BwdParams& p, const f32x4* gr, float mul, bool valid,
+                                                 const u32x2* xw, int pos, int grp, unsigned short* orow) {
+  constexpr int NB = D / 16;
+  if (!xw) {
+    if (valid) {
+#pragma unroll
+      for (int db = 0; db < NB; ++db)
+        *(u32x2*)(orow + 16 * db + 4 * grp) =
+            (u32x2){pk_bf16(gr[db][0] * mul, gr[db][1] * mul), pk_bf16(gr[db][2] * mul, gr[db][3] * mul)};
+    }
+    return;
+  }
+  const bool pos_ok = pos >= 0 && pos < p.T_rope;
+  const int tp = (valid && pos_ok) ? pos : 0;
+  float x[NB][4], u[NB][4];
+#pragma unroll
+  for (int db = 0; db < NB; ++db) {
+    x[db][0] = __builtin_bit_cast(float, xw[db][0] << 16);
+    x[db][1] = __builtin_bit_cast(float, xw[db][0] & 0xffff0000u);
+    x[db][2] = __builtin_bit_cast(float, xw[db][1] << 16);
+    x[db][3] = __builtin_bit_cast(float, xw[db][1] & 0xffff0000u);
+  }
+  // u = R(-theta) dy over the pairs (i, i + D/2): block db < NB/2 pairs with db + NB/2
+#pragma unroll
+  for (int db = 0; db < NB / 2; ++db) {
+    const int i = 16 * db + 4 * grp;  // < D/2
+    const f32x4 c4 = *(const f32x4*)(p.cos_tab + (size_t)tp * (D / 2) + i);
+    const f32x4 s4 = *(const f32x4*)(p.sin_tab + (size_t)tp * (D / 2) + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float a = gr[db][e] * mul, b = gr[db + NB / 2][e] * mul;
+      u[db][e] = fmaf(a, c4[e], b * s4[e]);
+      u[db + NB / 2][e] = fmaf(b, c4[e], -a * s4[e]);
+    }
+  }
+  float ss = 0.f, xu = 0.f;
+#pragma unroll
+  for (int db = 0; db < NB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      ss = fmaf(x[db][e], x[db][e], ss);
+      xu = fmaf(x[db][e], u[db][e], xu);
+    }
+  ss = sum_mod<16>(ss);
+  xu = sum_mod<16>(xu);
+  const float inv_r = 1.0f / sqrtf(ss * (1.0f / D) + p.eps);
+  const float k3 = xu * inv_r * inv_r * inv_r * (1.0f / D);
+  if (valid) {
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = pos_ok ? fmaf(u[db][e], inv_r, -x[db][e] * k3) : NAN;
+      *(u32x2*)(orow + 16 * db + 4 * grp) = (u32x2){pk_bf16(o[0], o[1]), pk_bf16(o[2], o[3])};
+    }
+  }
+}
+
+template <int D, bool PAIRED>
+__global__ __launch_bounds__(BWD16_THREADS, 2) void attn_bwd_dkdv16_kernel(BwdParams p) {
+  constexpr int NC = D / 8;   // chunks per row of the q/dO tiles (swizzled)
+  constexpr int NK = D / 32;  // k-steps of S and dP
+  constexpr int NB = D / 16;  // 16-wide blocks of d in dK^T, dV^T
+  constexpr int NW = K16_WAVES;
+  constexpr int BN = K16_BN, BM = K16_BM;
+  constexpr int QT = BM * D;
+  constexpr int RPI = 64 / NC;
+  constexpr int QIPW = BM / RPI / NW;  // copy instructions per wave per tensor
+  static_assert(QIPW >= 1 && BN == 16 * NW && BM == 64, "tile/wave mismatch");
+  __shared__ __attribute__((aligned(16))) unsigned short q_lds[NBUF][QT];
+  __shared__ __attribute__((aligned(16))) unsigned short do_lds[NBUF][QT];
+  __shared__ __attribute__((aligned(16))) float lse2_lds[NBUF][BM];
+  __shared__ __attribute__((aligned(16))) float dl_lds[NBUF][BM];
+
+  const int T = p.T;
+  const int nkt = (T + BN - 1) / BN;
+  const int nunit = PAIRED ? (nkt + 1) / 2 : nkt;
+  const int N = nunit * p.Hkv * p.B;
+  const int logical = xcd_remap(blockIdx.x, N);
+  const int bg = logical / nunit;
+  const int r_pair = logical - bg * nunit;
+  const int b = bg / p.Hkv, g = bg - b * p.Hkv;
+  const int G = p.H / p.Hkv;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int grp = lane >> 4, t16 = lane & 15;
+
+  const unsigned qrs = (unsigned)(p.H * D);
+  const unsigned kvrs = (unsigned)(p.Hkv * D);
+  const unsigned short* kp = (const unsigned short*)p.k + (size_t)b * T * kvrs + (size_t)g * D;
+  const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * T * kvrs + (size_t)g * D;
+
+  const bool full = p.window <= 0;
+  const int win = p.window;
+  const unsigned wlim = full ? 0x80000000u : (unsigned)win;
+
+  // ---- per-lane constant LDS offsets (the swizzle depends on row % 16, so
+  // +16 rows and +32 rows are plain element offsets) ----
+  // q/dO operand rows t (+16 qb + 32 ib) at column 32 ks + 8 g
+  int aoff[NK];
+#pragma unroll
+  for (int ks = 0; ks < NK; ++ks) aoff[ks] = swz_off<NC>(t16, 32 * ks + 8 * grp);
+  // transpose reads of dO^T / Q^T: rows 4 g + t/4 (+16) (+32 ib), columns 16 db + 4 (t % 4)
+  int toff[NB];
+#pragma unroll
+  for (int db = 0; db < NB; ++db) toff[db] = swz_off<NC>(4 * grp + (t16 >> 2), 16 * db + 4 * (t16 & 3));
+
+  // ---- q/dO tile and row-statistics copies (buffer -> LDS) ----
+  unsigned ld_off[QIPW];
+  int ld_row[QIPW], ld_ch[QIPW];
+#pragma unroll
+  for (int n = 0; n < QIPW; ++n) {
+    const int row = (wave * QIPW + n) * RPI + lane / NC;
+    ld_row[n] = row;
+    ld_ch[n] = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
+    ld_off[n] = (unsigned)(row * qrs + ld_ch[n] * 8) * 2u;
+  }
+  const unsigned qspan = (unsigned)(((size_t)(T - 1) * qrs + D) * 2);
+  auto run = [&](int kt) __attribute__((always_inline)) {
+    const int j0 = kt * BN;
+    const int kw = j0 + wave * 16;
+    const int kj = kw + t16;  // this lane's key
+    const size_t krow = ((size_t)b * T + kj) * kvrs + (size_t)g * D;  // its row of k, dk, dv
+    u32x2 xk[NB];  // its raw k row (prologue backward), loaded during the last step
+    const int i_last = full ? T - 1 : min(T - 1, j0 + BN - 1 + win - 1);
+    const int it_begin = j0 / BM, n_it = i_last / BM - it_begin + 1;
+    const int n_steps = G * n_it;
+    // K and V fragments of this lane's key as B operands: x[kj][32 ks + 8 g + e]
+    bf16x8 kf[NK], vf[NK];
+    f32x4 dk[NB], dv[NB];
+#pragma unroll
+    for (int ks = 0; ks < NK; ++ks) {
+      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
+      if (kj < T) {
+        a = *(const u32x4*)(kp + (size_t)kj * kvrs + 32 * ks + 8 * grp);
+        c = *(const u32x4*)(vp + (size_t)kj * kvrs + 32 * ks + 8 * grp);
+      }
+      kf[ks] = __builtin_bit_cast(bf16x8, a);
+      vf[ks] = __builtin_bit_cast(bf16x8, c);
+    }
+#pragma unroll
+    for (int db = 0; db < NB; ++db) {
+      dk[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      dv[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    auto issue_step = [&](int step, int buf) {
+      const int hq = step / n_it;
+      const int i0 = (it_begin + step - hq * n_it) * BM;
+      const int h = g * G + hq;
+      const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
+      const unsigned short* dop = (const unsigned short*)p.dout + (size_t)b * T * qrs + (size_t)h * D;
+      const BufDesc qrsr = buf_desc(qp, qspan), orsr = buf_desc(dop, qspan);
+      if (i0 + BM <= T) {
+        const unsigned so = (unsigned)i0 * qrs * 2u;
+#pragma unroll
+        for (int n = 0; n < QIPW; ++n) {
+          dma16(qrsr, ld_off[n], so, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
+          dma16(orsr, ld_off[n], so, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
+        }
+      } else {
+#pragma unroll
+        for (int n = 0; n < QIPW; ++n) {
+          const int i = min(i0 + ld_row[n], T - 1);
+          const unsigned vo = (unsigned)(i * qrs + ld_ch[n] * 8) * 2u;
+          dma16(qrsr, vo, 0u, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
+          dma16(orsr, vo, 0u, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
+        }
+      }
+      if (wave < 2) {  // per-row statistics: wave 0 lse2, wave 1 delta (rows past T clamped)
+        const float* src = (wave == 0 ? p.lse2 : p.delta) + ((size_t)b * p.H + h) * T;
+        const int i = min(i0 + lane, T - 1);
+        dma4(buf_desc(src, (unsigned)T * 4u), (unsigned)i * 4u, 0u, lds_u32(wave == 0 ? lse2_lds[buf] : dl_lds[buf]));
+      }
+    };
+
+    // Copies run NBUF - 1 steps ahead; vector memory operations complete in
+    // issue order, so the wait at the top of a step leaves exactly the later
+    // steps' copies in flight.
+    const int dma_ops = 2 * QIPW + (wave < 2 ? 1 : 0);
+    auto step_fn = [&](int step, auto bufc) __attribute__((always_inline)) {
+      constexpr int buf = decltype(bufc)::value;
+      const int hq = step / n_it;
+      const int i0 = (it_begin + step - hq * n_it) * BM;
+      wait_vmem_upto(dma_ops * (min(n_steps - 1, step + NBUF - 2) - step));
+      lds_barrier();  // this step's tiles landed everywhere; the oldest buffer is free
+      if (step + NBUF - 1 < n_steps) issue_step(step + NBUF - 1, (buf + NBUF - 1) % NBUF);
+      if (p.k_raw && step == n_steps - 1) {  // raw k row for the prologue backward
+#pragma unroll
+        for (int db = 0; db < NB; ++db)
+          xk[db] = kj < T ? *(const u32x2*)((const unsigned short*)p.k_raw + krow + 16 * db + 4 * grp)
+                          : (u32x2){0u, 0u};
+      }
+      const bool any = (kw <= i0 + BM - 1) && (full || kw + 15 > i0 - win);
+      if (!any) return;
+      const bool interior = (kw + 15 <= i0) && (full || kw > i0 + BM - 1 - win) && (i0 + BM <= T);
+      const unsigned short* ql = q_lds[buf];
+      const unsigned short* ol = do_lds[buf];
+#pragma unroll
+      for (int ib = 0; ib < BM / 32; ++ib) {
+        const int rb = 32 * ib * D;
+        // S and dP for queries 32 ib .. 32 ib + 31 (two 16-query blocks)
+        f32x4 sacc[2], dpacc[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          sacc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+          dpacc[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+        for (int ks = 0; ks < NK; ++ks)
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            const bf16x8 aq = *(const bf16x8*)(ql + aoff[ks] + rb + 16 * qb * D);
+            const bf16x8 ad = *(const bf16x8*)(ol + aoff[ks] + rb + 16 * qb * D);
+            sacc[qb] = mfma16(aq, kf[ks], sacc[qb]);
+            dpacc[qb] = mfma16(ad, vf[ks], dpacc[qb]);
+          }
+        // sacc[qb][r] = S[query i0 + 32 ib + 16 qb + 4 g + r][key kj]
+        f32x4 l4[2], d4[2];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+          l4[qb] = *(const f32x4*)(&lse2_lds[buf][32 * ib + 16 * qb + 4 * grp]);
+          d4[qb] = *(const f32x4*)(&dl_lds[buf][32 * ib + 16 * qb + 4 * grp]);
+        }
+        unsigned pw[4], sw[4];  // P and dS as bf16 pairs: B operands over the 32 queries
+        auto probs = [&](auto maskc) __attribute__((always_inline)) {
+          constexpr bool MASK = decltype(maskc)::value;
+          const int mbase = i0 + 32 * ib + 4 * grp - kj;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb) {
+            float pr[4], dsr[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              float pv = exp2_fast(fmaf(sacc[qb][e], p.scale_log2, -l4[qb][e]));
+              if (MASK) {
+                const bool vis =
+                    ((unsigned)(mbase + 16 * qb + e) < wlim) && (i0 + 32 * ib + 16 * qb + 4 * grp + e < T);
+                pv = vis ? pv : 0.f;
+              }
+              pr[e] = pv;
+              dsr[e] = pv * (dpacc[qb][e] - d4[qb][e]);
+            }
+            pw[2 * qb] = pk_bf16(pr[0], pr[1]);
+            pw[2 * qb + 1] = pk_bf16(pr[2], pr[3]);
+            sw[2 * qb] = pk_bf16(dsr[0], dsr[1]);
+            sw[2 * qb + 1] = pk_bf16(dsr[2], dsr[3]);
+          }
+        };
+        if (interior)
+          probs(std::integral_constant<bool, false>{});
+        else
+          probs(std::integral_constant<bool, true>{});
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, (u32x4){pw[0], pw[1], pw[2], pw[3]});
+        const bf16x8 sb = __builtin_bit_cast(bf16x8, (u32x4){sw[0], sw[1], sw[2], sw[3]});
+        // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries
+#pragma unroll
+        for (int db = 0; db < NB; ++db) {
+          const bf16x8 ot = cat_bf16x8(lds_read_tr16(ol + toff[db] + rb), lds_read_tr16(ol + toff[db] + rb + 16 * D));
+          const bf16x8 qt = cat_bf16x8(lds_read_tr16(ql + toff[db] + rb), lds_read_tr16(ql + toff[db] + rb + 16 * D));
+          dv[db] = mfma16(ot, pb, dv[db]);
+          dk[db] = mfma16(qt, sb, dk[db]);
+        }
+      }
+    };
+#pragma unroll
+    for (int s = 0; s < NBUF - 1; ++s)
+      if (s < n_steps) issue_step(s, s);
+    for (int step = 0; step < n_steps; step += NBUF) {
+      step_fn(step, std::integral_constant<int, 0>{});
+      if constexpr (NBUF > 1)
+        if (step + 1 < n_steps) step_fn(step + 1, std::integral_constant<int, 1 % NBUF>{});
+      if constexpr (NBUF > 2)
+        if (step + 2 < n_steps) step_fn(step + 2, std::integral_constant<int, 2 % NBUF>{});
+    }
+
+    store_grad_row16<D>(p, dv, 1.0f, kj < T, nullptr, 0, grp, (unsigned short*)p.dv + krow);
+    store_grad_row16<D>(p, dk, p.scale, kj < T, p.k_raw ? xk : nullptr, kj + (p.pos_offset ? p.pos_offset[b] : 0),
+                        grp, (unsigned short*)p.dk + krow);
+  };
+
+  run(r_pair);
+  if (PAIRED && nkt - 1 - r_pair > r_pair) {
+    lds_barrier();  // every wave is done with the last step's tiles before they are reloaded
+    run(nkt - 1 - r_pair);
+  }
+}
+
+// --------------------------------------------------------------------------
 // dQ: one workgroup per (b, h, 128-query tile), 4 waves of 32 queries; K/V
 // tiles of 64 keys stream through double-buffered LDS as in the forward.
 template <int D>
@@ -743,11 +1056,11 @@ hipError_t launch_bf16(const BwdParams& p, hipStream_t s, const BwdEvents& ev) {
   attn_bwd_dq_kernel<D><<<nqt * p.H * p.B, BWD_THREADS, 0, s>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if ((e = record(ev.dkdv_begin, s)) != hipSuccess) return e;
-  const int nkt = (p.T + BWD_BN - 1) / BWD_BN;
+  const int nkt = (p.T + K16_BN - 1) / K16_BN;
   if (p.window <= 0)
-    attn_bwd_dkdv_kernel<D, true><<<(nkt + 1) / 2 * p.Hkv * p.B, BWD_THREADS, 0, s>>>(p);
+    attn_bwd_dkdv16_kernel<D, true><<<(nkt + 1) / 2 * p.Hkv * p.B, BWD16_THREADS, 0, s>>>(p);
   else
-    attn_bwd_dkdv_kernel<D, false><<<nkt * p.Hkv * p.B, BWD_THREADS, 0, s>>>(p);
+    attn_bwd_dkdv16_kernel<D, false><<<nkt * p.Hkv * p.B, BWD16_THREADS, 0, s>>>(p);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return record(ev.end, s);
 }

@@ -238,6 +238,13 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16x16x32 bf16 MFMA, fp32 accumulate (lane l, t = l % 16, g = l / 16):
+// A[m = t][k = 8g + e], B[k = 8g + e][n = t], e = 0..7; result element r of
+// lane l is C[4g + r][t].
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // LDS tile layout: rows of NC 16-byte chunks (NC = elements per row / 8), no
 // padding; chunk c of row r is stored at chunk position c ^ swz<NC>(r). The
 // permutation makes both access patterns the kernels use conflict-free on
