@@ -22,15 +22,16 @@
 //         exchanged with dkdv, which keeps dQ free of float atomics. It
 //         forms the row statistics delta_i = <dout_i, out_i> and
 //         lse_i * log2(e) itself and stores them for dkdv.
-//   dkdv: one workgroup per (b, kv head, 128-key tile); each of the 4 waves
-//         keeps 32 keys' K and V fragments in registers and accumulates dK^T
-//         and dV^T for them over every query head of the GQA group and every
-//         128-query tile that intersects the band. S = Q K^T and dP = dO V^T
-//         come out with one key column per lane, which is directly the
-//         B-operand layout of dV^T += dO^T P and dK^T += Q^T dS; dO^T and
-//         Q^T are LDS transpose reads. Q/dO tiles and the per-row
-//         statistics stream into LDS with buffer-to-LDS loads running
-//         NBUF - 1 steps ahead; LDS addresses are per-lane constants.
+//   dkdv: one workgroup per (b, kv head, 64-key tile), two per CU; each of
+//         its 4 waves keeps 16 keys' K and V fragments in registers and
+//         accumulates dK^T and dV^T for them over every query head of the
+//         GQA group and every 64-query tile that intersects the band, on
+//         16x16x32 MFMA. S = Q K^T and dP = dO V^T come out with one key
+//         column per lane, which is directly the B-operand layout of
+//         dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T are LDS transpose
+//         reads. Q/dO tiles and the per-row statistics stream into LDS with
+//         buffer-to-LDS loads running NBUF - 1 steps ahead; LDS addresses are
+//         per-lane constants.
 // f32 path: row statistics, then plain per-query (dq) and per-key (dk, dv)
 // loops in float32.
 
@@ -44,8 +45,6 @@
 namespace nc {
 namespace {
 
-constexpr int BWD_BN = 128;  // keys per workgroup (32 per wave)
-constexpr int BWD_BM = 128;  // queries per step
 constexpr int BWD_THREADS = 256;
 constexpr int NBUF = 2;  // q/dO tile buffers: loads run one step ahead
 constexpr int DQ_BM = 128;  // queries per dq workgroup (32 per wave)
@@ -177,261 +176,12 @@ __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(BwdParams p) {
 }
 
 // --------------------------------------------------------------------------
-// dK and dV: one workgroup per (b, kv head, 128-key tile), 4 waves of 32 keys.
-template <int D, bool PAIRED>
-__global__ __launch_bounds__(BWD_THREADS, 1) void attn_bwd_dkdv_kernel(BwdParams p) {
-  constexpr int NC = D / 8;  // chunks per row of the q/dO tiles (swizzled)
-  constexpr int NS = D / 16;
-  constexpr int ND = D / 32;
-  constexpr int QT = BWD_BM * D;          // elements of one q or dO tile
-  constexpr int RPI = 64 / NC;            // tile rows per direct-to-LDS instruction
-  constexpr int QIPW = BWD_BM / RPI / 4;  // such instructions per wave per tensor
-  static_assert(QIPW >= 1, "tile/wave mismatch");
-  __shared__ __attribute__((aligned(16))) unsigned short q_lds[NBUF][QT];
-  __shared__ __attribute__((aligned(16))) unsigned short do_lds[NBUF][QT];
-  __shared__ __attribute__((aligned(16))) float lse2_lds[NBUF][BWD_BM];
-  __shared__ __attribute__((aligned(16))) float dl_lds[NBUF][BWD_BM];
-
-  // Under the full causal mask a workgroup takes key tiles r and nkt-1-r of
-  // one (b, kv head), in that order (their query counts add up to the same
-  // for every r: equal weight, no tail); else one key tile, early first.
-  const int T = p.T;
-  const int nkt = (T + BWD_BN - 1) / BWD_BN;
-  const int nunit = PAIRED ? (nkt + 1) / 2 : nkt;
-  const int N = nunit * p.Hkv * p.B;
-  const int logical = xcd_remap(blockIdx.x, N);
-  const int bg = logical / nunit;
-  const int r_pair = logical - bg * nunit;
-  const int b = bg / p.Hkv, g = bg - b * p.Hkv;
-  const int G = p.H / p.Hkv;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-  const int li = lane & 31, hh = lane >> 5;
-  const int grp = lane >> 4, t16 = lane & 15;
-
-  const unsigned qrs = (unsigned)(p.H * D);
-  const unsigned kvrs = (unsigned)(p.Hkv * D);
-  const unsigned short* kp = (const unsigned short*)p.k + (size_t)b * T * kvrs + (size_t)g * D;
-  const unsigned short* vp = (const unsigned short*)p.v + (size_t)b * T * kvrs + (size_t)g * D;
-
-  const int tr_row = t16 >> 2;
-  const int tr_col = 16 * (grp & 1) + 4 * (t16 & 3);
-
-  const bool full = p.window <= 0;
-  const int win = p.window;
-  const unsigned wlim = full ? 0x80000000u : (unsigned)win;
-
-  // ---- per-lane constant LDS offsets ----
-  // q/dO operand rows li (+32 ib) at chunk 2 st + hh
-  int aoff[NS];
-#pragma unroll
-  for (int st = 0; st < NS; ++st) aoff[st] = swz_off<NC>(li, 16 * st + 8 * hh);
-  // transpose reads of dO^T / Q^T: rows 4 hh + t16/4 (+8) (+16 u + 32 ib), columns 32 d + tr_col
-  int toff1[ND], toff2[ND];
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    toff1[d] = swz_off<NC>(4 * hh + tr_row, 32 * d + tr_col);
-    toff2[d] = swz_off<NC>(4 * hh + tr_row + 8, 32 * d + tr_col);
-  }
-
-  // ---- q/dO tile and row-statistics copies (buffer -> LDS) ----
-  unsigned ld_off[QIPW];
-  int ld_row[QIPW], ld_ch[QIPW];
-#pragma unroll
-  for (int n = 0; n < QIPW; ++n) {
-    const int row = (wave * QIPW + n) * RPI + lane / NC;
-    ld_row[n] = row;
-    ld_ch[n] = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
-    ld_off[n] = (unsigned)(row * qrs + ld_ch[n] * 8) * 2u;
-  }
-  const unsigned qspan = (unsigned)(((size_t)(T - 1) * qrs + D) * 2);
-  auto run = [&](int kt) __attribute__((always_inline)) {
-    const int j0 = kt * BWD_BN;
-    const int kw = j0 + wave * 32;
-    const int kj = kw + li;  // this lane's key
-    const size_t krow = ((size_t)b * T + kj) * kvrs + (size_t)g * D;  // its row of k, dk, dv
-    u32x2 xk[ND * 4];  // its raw k row (prologue backward), loaded during the last step
-    const int i_last = full ? T - 1 : min(T - 1, j0 + BWD_BN - 1 + win - 1);
-    const int it_begin = j0 / BWD_BM, n_it = i_last / BWD_BM - it_begin + 1;
-    const int n_steps = G * n_it;
-    // K and V fragments of this lane's key: lane (li, hh) holds x[kj][16 s + 8 hh + e].
-    bf16x8 kf[NS], vf[NS];
-    f32x16 dk[ND], dv[ND];
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      u32x4 a = {0u, 0u, 0u, 0u}, c = {0u, 0u, 0u, 0u};
-      if (kj < T) {
-        a = *(const u32x4*)(kp + (size_t)kj * kvrs + 16 * s + 8 * hh);
-        c = *(const u32x4*)(vp + (size_t)kj * kvrs + 16 * s + 8 * hh);
-      }
-      kf[s] = __builtin_bit_cast(bf16x8, a);
-      vf[s] = __builtin_bit_cast(bf16x8, c);
-    }
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      dk[d] = (f32x16){};
-      dv[d] = (f32x16){};
-    }
-    auto issue_step = [&](int step, int buf) {
-      const int hq = step / n_it;
-      const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
-      const int h = g * G + hq;
-      const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
-      const unsigned short* dop = (const unsigned short*)p.dout + (size_t)b * T * qrs + (size_t)h * D;
-      const BufDesc qrsr = buf_desc(qp, qspan), orsr = buf_desc(dop, qspan);
-      if (i0 + BWD_BM <= T) {
-        const unsigned so = (unsigned)i0 * qrs * 2u;
-#pragma unroll
-        for (int n = 0; n < QIPW; ++n) {
-          dma16(qrsr, ld_off[n], so, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
-          dma16(orsr, ld_off[n], so, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
-        }
-      } else {
-#pragma unroll
-        for (int n = 0; n < QIPW; ++n) {
-          const int i = min(i0 + ld_row[n], T - 1);
-          const unsigned vo = (unsigned)(i * qrs + ld_ch[n] * 8) * 2u;
-          dma16(qrsr, vo, 0u, lds_u32(&q_lds[buf][(wave * QIPW + n) * RPI * D]));
-          dma16(orsr, vo, 0u, lds_u32(&do_lds[buf][(wave * QIPW + n) * RPI * D]));
-        }
-      }
-      {  // per-row statistics: waves 0/2 lse2, waves 1/3 delta, 64 rows each (rows past T clamped)
-        const bool isl = (wave & 1) == 0;
-        const int r0 = (wave >> 1) * 64;
-        const float* src = (isl ? p.lse2 : p.delta) + ((size_t)b * p.H + h) * T;
-        const int i = min(i0 + r0 + lane, T - 1);
-        dma4(buf_desc(src, (unsigned)T * 4u), (unsigned)i * 4u, 0u, lds_u32((isl ? lse2_lds[buf] : dl_lds[buf]) + r0));
-      }
-    };
-
-    // Copies run NBUF - 1 steps ahead. Vector memory operations complete in
-    // issue order, so the wait at the top of a step lets exactly the copies of
-    // the later steps already issued stay in flight.
-    const int dma_ops = 2 * QIPW + 1;  // copies this wave issues per step
-    auto step_fn = [&](int step, auto bufc) __attribute__((always_inline)) {
-      constexpr int buf = decltype(bufc)::value;
-      const int hq = step / n_it;
-      const int i0 = (it_begin + step - hq * n_it) * BWD_BM;
-      wait_vmem_upto(dma_ops * (min(n_steps - 1, step + NBUF - 2) - step));
-      lds_barrier();  // this step's tiles landed everywhere; the oldest buffer is free
-      if (step + NBUF - 1 < n_steps) issue_step(step + NBUF - 1, (buf + NBUF - 1) % NBUF);
-      // the raw k row for the prologue backward, requested during the last step
-      if (p.k_raw && step == n_steps - 1) load_row_words<D>((const unsigned short*)p.k_raw + krow, kj < T, hh, xk);
-      const bool any = (kw <= i0 + BWD_BM - 1) && (full || kw + 31 > i0 - win);
-      if (!any) return;
-      const bool interior = (kw + 31 <= i0) && (full || kw > i0 + BWD_BM - 1 - win) && (i0 + BWD_BM <= T);
-      const unsigned short* ql = q_lds[buf];
-      const unsigned short* ol = do_lds[buf];
-#pragma unroll
-      for (int ib = 0; ib < BWD_BM / 32; ++ib) {
-        // Every LDS operand of this 32-query half is requested before the
-        // first product: q and dO rows (S, dP), the row statistics, and the
-        // dO^T / Q^T transpose reads (dV, dK).
-        bf16x8 aq[NS], ad[NS];
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          aq[st] = *(const bf16x8*)(ql + aoff[st] + 32 * ib * D);
-          ad[st] = *(const bf16x8*)(ol + aoff[st] + 32 * ib * D);
-        }
-        f32x4 l4[4], d4[4];
-#pragma unroll
-        for (int rg = 0; rg < 4; ++rg) {
-          l4[rg] = *(const f32x4*)(&lse2_lds[buf][32 * ib + 8 * rg + 4 * hh]);
-          d4[rg] = *(const f32x4*)(&dl_lds[buf][32 * ib + 8 * rg + 4 * hh]);
-        }
-        bf16x8 ot[2][ND], qt[2][ND];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            const int rb = (32 * ib + 16 * u) * D;
-            ot[u][d] = cat_bf16x8(lds_read_tr16(ol + toff1[d] + rb), lds_read_tr16(ol + toff2[d] + rb));
-            qt[u][d] = cat_bf16x8(lds_read_tr16(ql + toff1[d] + rb), lds_read_tr16(ql + toff2[d] + rb));
-          }
-
-        f32x16 sacc = (f32x16){}, dpacc = (f32x16){};
-#pragma unroll
-        for (int st = 0; st < NS; ++st) {
-          sacc = mfma32(aq[st], kf[st], sacc);
-          dpacc = mfma32(ad[st], vf[st], dpacc);
-        }
-        // sacc[r] = S[query i0 + 32 ib + 8 (r/4) + 4 hh + r%4][key kj]
-        unsigned pw[8], sw[8];  // P and dS as bf16 pairs
-        auto probs = [&](auto maskc) {
-          constexpr bool MASK = decltype(maskc)::value;
-          const int mbase = i0 + 32 * ib + 4 * hh - kj;
-#pragma unroll
-          for (int rg = 0; rg < 4; ++rg) {
-            float pr[4], dsr[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 4 * rg + e;
-              float pv = exp2_fast(fmaf(sacc[r], p.scale_log2, -l4[rg][e]));
-              if (MASK) {
-                const int off = 8 * rg + e;
-                const bool vis = ((unsigned)(mbase + off) < wlim) && (i0 + 32 * ib + 8 * rg + 4 * hh + e < T);
-                pv = vis ? pv : 0.f;
-              }
-              pr[e] = pv;
-              dsr[e] = pv * (dpacc[r] - d4[rg][e]);
-            }
-            pw[2 * rg] = pk_bf16(pr[0], pr[1]);
-            pw[2 * rg + 1] = pk_bf16(pr[2], pr[3]);
-            sw[2 * rg] = pk_bf16(dsr[0], dsr[1]);
-            sw[2 * rg + 1] = pk_bf16(dsr[2], dsr[3]);
-          }
-        };
-        if (interior)
-          probs(std::integral_constant<bool, false>{});
-        else
-          probs(std::integral_constant<bool, true>{});
-        // dV^T += dO^T P and dK^T += Q^T dS over these 32 queries.
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 pq = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
-          const u32x4 sq = {sw[4 * u], sw[4 * u + 1], sw[4 * u + 2], sw[4 * u + 3]};
-          const bf16x8 pb = __builtin_bit_cast(bf16x8, pq);
-          const bf16x8 sb = __builtin_bit_cast(bf16x8, sq);
-#pragma unroll
-          for (int d = 0; d < ND; ++d) {
-            dv[d] = mfma32(ot[u][d], pb, dv[d]);
-            dk[d] = mfma32(qt[u][d], sb, dk[d]);
-          }
-        }
-      }
-    };
-#pragma unroll
-    for (int s = 0; s < NBUF - 1; ++s)
-      if (s < n_steps) issue_step(s, s);
-    for (int step = 0; step < n_steps; step += NBUF) {
-      step_fn(step, std::integral_constant<int, 0>{});
-      if constexpr (NBUF > 1)
-        if (step + 1 < n_steps) step_fn(step + 1, std::integral_constant<int, 1 % NBUF>{});
-      if constexpr (NBUF > 2)
-        if (step + 2 < n_steps) step_fn(step + 2, std::integral_constant<int, 2 % NBUF>{});
-    }
-
-    // dV, and dK (scaled; through the prologue backward when asked) for this lane's key.
-    store_grad_row<D>(p, dv, 1.0f, kj < T, nullptr, 0, hh, (unsigned short*)p.dv + krow);
-    store_grad_row<D>(p, dk, p.scale, kj < T, p.k_raw ? xk : nullptr, kj + (p.pos_offset ? p.pos_offset[b] : 0),
-                      hh, (unsigned short*)p.dk + krow);
-  };
-
-  run(r_pair);
-  if (PAIRED && nkt - 1 - r_pair > r_pair) {
-    lds_barrier();  // every wave is done with the last step's tiles before they are reloaded
-    run(nkt - 1 - r_pair);
-  }
-}
-
-// --------------------------------------------------------------------------
-// dK and dV with 16 keys per wave: one workgroup per (b, kv head, 64-key
-// tile), 4 waves, two workgroups per CU, 16x16x32 bf16 MFMA, 64-query steps.
-// The same products as the kernel above; halving each wave's keys halves its
-// stationary registers (K, V fragments and the dK, dV accumulators), so two
-// waves of independent workgroups share each SIMD and hide each other's LDS
-// and arithmetic latency. Layouts (lane l,
+// dK and dV: one workgroup per (b, kv head, 64-key tile), 4 waves of 16 keys,
+// two workgroups per CU, 16x16x32 bf16 MFMA, 64-query steps. With 16 keys a
+// wave's stationary registers (K, V fragments and the dK, dV accumulators)
+// leave room for two waves of independent workgroups on every SIMD, which
+// hide each other's LDS and arithmetic latency (32 keys per wave on
+// 32x32x16 MFMA allowed one). Layouts (lane l,
 // t = l % 16, g = l / 16): A operands hold A[t][8 g + e], B operands
 // B[8 g + e][t], results C[4 g + r][t].
 //   S = Q K^T per 16-query block: A = q rows (LDS), B = K^T (registers),
@@ -731,10 +481,11 @@ __global__ __launch_bounds__(BWD16_THREADS, 2) void attn_bwd_dkdv16_kernel(BwdPa
                         grp, (unsigned short*)p.dk + krow);
   };
 
-  run(r_pair);
-  if (PAIRED && nkt - 1 - r_pair > r_pair) {
-    lds_barrier();  // every wave is done with the last step's tiles before they are reloaded
-    run(nkt - 1 - r_pair);
+  // one copy of the tile code for both key tiles of a pair
+  const int n_pass = PAIRED && nkt - 1 - r_pair > r_pair ? 2 : 1;
+  for (int pass = 0; pass < n_pass; ++pass) {
+    if (pass) lds_barrier();  // every wave is done with the last step's tiles before they are reloaded
+    run(pass ? nkt - 1 - r_pair : r_pair);
   }
 }
 
