@@ -298,16 +298,17 @@ __global__ __launch_bounds__(BWD16_THREADS, 2) void attn_bwd_dkdv16_kernel(BwdPa
   const int win = p.window;
   const unsigned wlim = full ? 0x80000000u : (unsigned)win;
 
-  // ---- per-lane constant LDS offsets (the swizzle depends on row % 16, so
-  // +16 rows and +32 rows are plain element offsets) ----
+  // ---- per-lane constant LDS offsets (the tiles use the swz_kv
+  // permutation, which depends on row % 16, so +16 rows and +32 rows are
+  // plain element offsets) ----
   // q/dO operand rows t (+16 qb + 32 ib) at column 32 ks + 8 g
   int aoff[NK];
 #pragma unroll
-  for (int ks = 0; ks < NK; ++ks) aoff[ks] = swz_off<NC>(t16, 32 * ks + 8 * grp);
+  for (int ks = 0; ks < NK; ++ks) aoff[ks] = swz_kv_off<NC>(t16, 32 * ks + 8 * grp);
   // transpose reads of dO^T / Q^T: rows 4 g + t/4 (+16) (+32 ib), columns 16 db + 4 (t % 4)
   int toff[NB];
 #pragma unroll
-  for (int db = 0; db < NB; ++db) toff[db] = swz_off<NC>(4 * grp + (t16 >> 2), 16 * db + 4 * (t16 & 3));
+  for (int db = 0; db < NB; ++db) toff[db] = swz_kv_off<NC>(4 * grp + (t16 >> 2), 16 * db + 4 * (t16 & 3));
 
   // ---- q/dO tile and row-statistics copies (buffer -> LDS) ----
   unsigned ld_off[QIPW];
@@ -316,7 +317,7 @@ __global__ __launch_bounds__(BWD16_THREADS, 2) void attn_bwd_dkdv16_kernel(BwdPa
   for (int n = 0; n < QIPW; ++n) {
     const int row = (wave * QIPW + n) * RPI + lane / NC;
     ld_row[n] = row;
-    ld_ch[n] = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
+    ld_ch[n] = (lane % NC) ^ (swz_kv<NC>(row) & (NC - 1));
     ld_off[n] = (unsigned)(row * qrs + ld_ch[n] * 8) * 2u;
   }
   const unsigned qspan = (unsigned)(((size_t)(T - 1) * qrs + D) * 2);

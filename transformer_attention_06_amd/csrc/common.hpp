@@ -263,6 +263,24 @@ __device__ __forceinline__ int swz_off(int r, int col) {
   return r * (NC * 8) + ((((col >> 3) ^ swz<NC>(r)) & (NC - 1)) << 3) + (col & 7);
 }
 
+// The dK/dV kernel's q/dO tiles use another permutation: its operand reads
+// are 16 consecutive rows at one chunk (ds_read_b128, 16 lanes per cycle),
+// and its transpose reads cover 8 rows x one aligned pair of chunks per 32
+// lanes (ds_read_b64_tr_b16, 32 lanes of 8 bytes per cycle). The rows of
+// each 8-row half must then land on 8 distinct aligned chunk pairs of the
+// 64 banks, and 16 consecutive rows on 16 distinct chunks. Rows are
+// D * 2 bytes long, so NC < 16 rows share a 256-byte bank window.
+template <int NC>
+__device__ __forceinline__ int swz_kv(int r) {
+  if (NC >= 16) return 2 * (r & 7) + ((r >> 3) & 1);
+  if (NC == 8) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
+  return 2 * ((r >> 2) & 1) + ((r >> 3) & 1);
+}
+template <int NC>
+__device__ __forceinline__ int swz_kv_off(int r, int col) {
+  return r * (NC * 8) + ((((col >> 3) ^ swz_kv<NC>(r)) & (NC - 1)) << 3) + (col & 7);
+}
+
 // Blocks -> XCD-contiguous logical ids. Workgroups are dealt to the 8 XCDs
 // round-robin (block L runs on XCD L % 8); this maps the blocks that land on
 // one XCD to one contiguous range of logical ids so that neighbouring work
