@@ -264,15 +264,18 @@ __device__ __forceinline__ int swz_off(int r, int col) {
 }
 
 // The dK/dV kernel's q/dO tiles use another permutation: its operand reads
-// are 16 consecutive rows at one chunk (ds_read_b128, 16 lanes per cycle),
-// and its transpose reads cover 8 rows x one aligned pair of chunks per 32
-// lanes (ds_read_b64_tr_b16, 32 lanes of 8 bytes per cycle). The rows of
-// each 8-row half must then land on 8 distinct aligned chunk pairs of the
-// 64 banks, and 16 consecutive rows on 16 distinct chunks. Rows are
-// D * 2 bytes long, so NC < 16 rows share a 256-byte bank window.
+// are 16 consecutive rows at one chunk (ds_read_b128) and its transpose reads
+// cover 4 rows x 4 aligned 8-byte pieces per 16 lanes (ds_read_b64_tr_b16).
+// For 256-byte rows (NC = 16) the table below came out of a timed search
+// over bit permutations of the row index with one xor fold: it runs the
+// b128 pattern at the LDS peak (256 B/clk/CU, where a plain r & 15 xor also
+// does) and the transpose pattern at 189 B/clk/CU (the row-major xor gets
+// 128). As bits: chunk xor = (r3, r1, r2 ^ r3, r0 ^ r1). Rows of NC < 16
+// chunks share a 256-byte bank window and keep a simpler interleave.
 template <int NC>
 __device__ __forceinline__ int swz_kv(int r) {
-  if (NC >= 16) return 2 * (r & 7) + ((r >> 3) & 1);
+  if (NC >= 16)
+    return ((r >> 3) & 1) | (r & 2) | ((((r >> 2) ^ (r >> 3)) & 1) << 2) | (((r ^ (r >> 1)) & 1) << 3);
   if (NC == 8) return 2 * ((r >> 1) & 3) + ((r >> 3) & 1);
   return 2 * ((r >> 2) & 1) + ((r >> 3) & 1);
 }
