@@ -218,10 +218,12 @@ __device__ __forceinline__ float max_mod(float x) { return reduce_mod<S, true>(x
 // lane 4e + i/4 of its group. So if lane t points at row (r0 + t/4), column
 // (c0 + 4*(t%4)) of a row-major 16-bit matrix, lane i receives the column
 // c0 + i of rows r0 .. r0+3.
+// The pointer is cast to the LDS address space directly (not through an
+// integer), so the compiler sees base + constant and folds the constant into
+// the instruction's offset field instead of holding one address register per
+// read.
 __device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_addr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)((__attribute__((address_space(3))) char*)(
-          (size_t)lds_addr)));
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)lds_addr);
 }
 
 __device__ __forceinline__ bf16x8 cat_bf16x8(s16x4 a, s16x4 b) {
