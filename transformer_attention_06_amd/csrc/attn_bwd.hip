@@ -348,10 +348,20 @@ __global__ __launch_bounds__(BWD16_THREADS, 2) void attn_bwd_dkdv16_kernel(BwdPa
       dk[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
       dv[db] = (f32x4){0.f, 0.f, 0.f, 0.f};
     }
-    auto issue_step = [&](int step, int buf) {
-      const int hq = step / n_it;
-      const int i0 = (it_begin + step - hq * n_it) * BM;
-      const int h = g * G + hq;
+    // Steps run over (query head of the group, 64-query tile), tiles
+    // fastest. The copies and the compute each keep a running cursor over
+    // them (both advance one step per call, in order).
+    const int i0_first = it_begin * BM, i0_last = (it_begin + n_it - 1) * BM;
+    int cp_h = g * G, cp_i0 = i0_first;  // next step to copy
+    int cm_i0 = i0_first;                // next step to compute
+    auto issue_step = [&](int buf) {
+      const int h = cp_h, i0 = cp_i0;
+      if (cp_i0 == i0_last) {
+        cp_i0 = i0_first;
+        ++cp_h;
+      } else {
+        cp_i0 += BM;
+      }
       const unsigned short* qp = (const unsigned short*)p.q + (size_t)b * T * qrs + (size_t)h * D;
       const unsigned short* dop = (const unsigned short*)p.dout + (size_t)b * T * qrs + (size_t)h * D;
       const BufDesc qrsr = buf_desc(qp, qspan), orsr = buf_desc(dop, qspan);
@@ -384,11 +394,11 @@ __global__ __launch_bounds__(BWD16_THREADS, 2) void attn_bwd_dkdv16_kernel(BwdPa
     const int dma_ops = 2 * QIPW + (wave < 2 ? 1 : 0);
     auto step_fn = [&](int step, auto bufc) __attribute__((always_inline)) {
       constexpr int buf = decltype(bufc)::value;
-      const int hq = step / n_it;
-      const int i0 = (it_begin + step - hq * n_it) * BM;
+      const int i0 = cm_i0;
+      cm_i0 = cm_i0 == i0_last ? i0_first : cm_i0 + BM;
       wait_vmem_upto(dma_ops * (min(n_steps - 1, step + NBUF - 2) - step));
       lds_barrier();  // this step's tiles landed everywhere; the oldest buffer is free
-      if (step + NBUF - 1 < n_steps) issue_step(step + NBUF - 1, (buf + NBUF - 1) % NBUF);
+      if (step + NBUF - 1 < n_steps) issue_step((buf + NBUF - 1) % NBUF);
       if (p.k_raw && step == n_steps - 1) {  // raw k row for the prologue backward
 #pragma unroll
         for (int db = 0; db < NB; ++db)
@@ -468,7 +478,7 @@ __global__ __launch_bounds__(BWD16_THREADS, 2) void attn_bwd_dkdv16_kernel(BwdPa
     };
 #pragma unroll
     for (int s = 0; s < NBUF - 1; ++s)
-      if (s < n_steps) issue_step(s, s);
+      if (s < n_steps) issue_step(s);
     for (int step = 0; step < n_steps; step += NBUF) {
       step_fn(step, std::integral_constant<int, 0>{});
       if constexpr (NBUF > 1)
