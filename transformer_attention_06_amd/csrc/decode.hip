@@ -7,7 +7,9 @@
 // (B, T, H, D) cache, per-row int32 lengths; section 6: single-token decode
 // slices the key window.)
 //
-// decode_split: one wave per (chunk of cache positions, kv head, row). The
+// decode_split: one wave per (kv head, chunk of cache positions, row), kv
+//   heads fastest in the grid so that the waves dispatched together read the
+//   whole of each cache position (its Hkv head rows are contiguous). The
 //   wave's groups of D/8 lanes each take every NGR-th position of the chunk,
 //   so one load instruction reads NGR whole head vectors (256 bytes each at
 //   D = 128). All of a group's K and V rows are requested before any is used
@@ -73,7 +75,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   constexpr int CHUNK = NGR * KPG;        // positions per wave
   static_assert(CHUNK == decode_chunk(D, G), "chunk size mismatch");
 
-  const int sp = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int g = blockIdx.x, sp = blockIdx.y, b = blockIdx.z;
   const int L = p.seqlens[b];
   if (L < 1 || L > p.T_max) return;
   const bool full = p.window <= 0 || p.window >= L;
@@ -222,7 +224,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
 
 template <int D, int G, bool BF16>
 hipError_t launch_t(const DecodeParams& p, hipStream_t s) {
-  decode_split_kernel<D, G, BF16><<<dim3(p.n_split, p.Hkv, p.B), 64, 0, s>>>(p);
+  // kv heads fastest: the waves dispatched together read whole cache positions
+  decode_split_kernel<D, G, BF16><<<dim3(p.Hkv, p.n_split, p.B), 64, 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   decode_combine_kernel<D, G, BF16><<<dim3(p.H, p.B), D, 0, s>>>(p);
