@@ -12,6 +12,10 @@ kernels store dq and dk). The reported value is band-counted attention fwd+bwd F
 the prologue's time counts against it. The decode workload (64 rows, one
 query each, cache lengths uniform on 1..2048, same 20-layer schedule) is
 timed as a separate phase and reported in GB/s of algorithmic bytes.
+After the timed steps the same steps run twice more: once with events
+between the kernels (per-kernel times) and once beside a one-wave probe on
+a second stream that reads the shader clock they run at (`sclk_mhz`, and
+the roofline fraction at that clock next to the nominal one).
 
 Inputs are seeded N(0, 1) bf16 tensors drawn on the device and resident in
 HBM before the timed region. Prints one JSON line on stdout; progress goes
@@ -26,6 +30,7 @@ import sys
 import time
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+NOMINAL_SCLK_MHZ = 2400.0  # the shader clock that peak is quoted at
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd+bwd TFLOP/s (band-counted) at d20 T=2048; decode GB/s"
 
@@ -171,15 +176,31 @@ def main():
         step()
     torch.cuda.synchronize()
     # whole-step timing: nothing but the work between the two events
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # (an event after every step, for the spread of step times)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    t0.record()
+    marks[0].record()
+    for i in range(args.steps):
+        step()
+        marks[i + 1].record()
+    torch.cuda.synchronize()
+    ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)  # for the phases below
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+    spread = {q: round(float(np.percentile(per_step, pc)), 4) for q, pc in (("p10", 10), ("median", 50), ("p90", 90))}
+    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, per step {json.dumps(spread)}")
+    # The shader clock while the same steps run again: a one-wave probe on a
+    # second stream that reads the shader-cycle and 100 MHz counters.
+    side = torch.cuda.Stream()
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    native.nc_measure_shader_clock(max(1, min(10000, int(0.9 * ms_step * args.steps))), out=clk, stream=side)
     for _ in range(args.steps):
         step()
-    t1.record()
     torch.cuda.synchronize()
-    ms_step = t0.elapsed_time(t1) / args.steps
-    log(f"timed {args.steps} steps: {ms_step:.3f} ms/step")
+    cyc, ticks = (int(x) for x in clk.cpu())
+    sclk_mhz = cyc / ticks * 100.0 if ticks else None
+    log(f"shader clock during the steps: {sclk_mhz and round(sclk_mhz)} MHz")
     # per-kernel timing in a second pass of the same steps (events between launches)
     tm = Timer(torch)
     for _ in range(args.steps):
@@ -322,6 +343,10 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": tr["bytes"] if tr else None,
                 "traffic_split": tr,
+                "sclk_mhz": round(sclk_mhz, 1) if sclk_mhz else None,
+                "peak_at_sclk": round(PEAK_BF16_TFLOPS * sclk_mhz / NOMINAL_SCLK_MHZ, 1) if sclk_mhz else None,
+                "frac_at_sclk": round(achieved / (PEAK_BF16_TFLOPS * sclk_mhz / NOMINAL_SCLK_MHZ), 4)
+                if sclk_mhz else None,
                 "note": "achieved = band-counted flops per launch (per visible pair: 4*D fwd, "
                         "8*D dK/dV kernel, 6*D dQ kernel; B*H*pairs(T,w) pairs) / average launch "
                         "time, averaged over the 20 layers"}
@@ -334,6 +359,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "ms_per_step_spread": spread, "sclk_mhz": round(sclk_mhz, 1) if sclk_mhz else None,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16, drawn on the device)",
         "config": {"workload": "d20_bf16: B=32 T=2048 H=Hkv=10 D=128, 20 layers SSSL "

@@ -304,6 +304,17 @@ nc_status nc_attn_fwd_prologue(nc_dtype dt, int B, int T, int H, int Hkv, int D,
 nc_status nc_profile_fwd_prologue(void* prologue_begin, void* fwd_begin, void* end);
 
 /*
+ * Measurement aid: launches one wave on `stream` that runs for `milliseconds`
+ * of wall time (by the GPU's constant 100 MHz counter) and then writes
+ * out[0] = shader-clock cycles and out[1] = 100 MHz ticks that passed, as
+ * uint64 to DEVICE memory `out` (2 values, caller-owned). Enqueued on a
+ * second stream while other kernels run, out[0] / out[1] * 100 MHz is the
+ * average shader clock they ran at; the wave sleeps between counter reads.
+ * NC_ERR_INVALID_ARG for a NULL out or milliseconds outside 1..10000.
+ */
+nc_status nc_measure_shader_clock(unsigned long long* out, int milliseconds, nc_stream stream);
+
+/*
  * QK prologue backward: given dq_out, dk_out (gradients w.r.t. the prologue
  * outputs) and the raw q, k, writes dq, dk w.r.t. the raw inputs:
  *   u = R(-theta) dy,  r = sqrt(mean x^2 + eps),  dx = u / r - x <x, u> / (D r^3).

@@ -169,6 +169,14 @@ def test_profile_hook_validation(L):
     assert L.nc_profile_bwd_main(None, None, None) == OK
 
 
+def test_clock_probe_validation(L):
+    assert L.nc_measure_shader_clock(None, 10, None) == INVALID
+    assert "out" in msg(L)
+    assert L.nc_measure_shader_clock(A, 0, None) == INVALID
+    assert L.nc_measure_shader_clock(A, 10001, None) == INVALID
+    assert "milliseconds" in msg(L)
+
+
 def test_error_message_is_per_thread(L):
     import threading
     assert fwd(L, q=None) == INVALID

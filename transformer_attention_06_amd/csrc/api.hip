@@ -457,6 +457,16 @@ nc_status nc_profile_fwd_prologue(void* prologue_begin, void* fwd_begin, void* e
   return NC_OK;
 }
 
+nc_status nc_measure_shader_clock(unsigned long long* out, int milliseconds, nc_stream stream) {
+  NC_TRY(check_ptr(out, "out"));
+  if (milliseconds < 1 || milliseconds > 10000)
+    return fail(NC_ERR_INVALID_ARG, "milliseconds=%d outside 1..10000", milliseconds);
+  NC_TRY(check_device(nullptr));
+  hipStream_t s = (hipStream_t)stream;
+  return finish(nc::launch_shader_clock(out, 100000ull * (unsigned long long)milliseconds, s), s,
+                "nc_measure_shader_clock");
+}
+
 nc_status nc_qk_prologue_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const void* q, const void* k,
                              const int32_t* pos_offset, const float* cos_tab, const float* sin_tab, int T_rope,
                              float eps, void* q_out, void* k_out, nc_stream stream) {

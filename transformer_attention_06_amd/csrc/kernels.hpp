@@ -115,6 +115,10 @@ struct AppendParams {
 constexpr int decode_keys_per_group(int G) { return G <= 2 ? 16 : (G <= 4 ? 8 : 4); }
 constexpr int decode_chunk(int D, int G) { return (64 / (D / 8)) * decode_keys_per_group(G); }
 
+// Average shader clock: out[0] shader cycles and out[1] 100 MHz ticks over
+// `ticks` ticks of wall time (device memory, 2 values).
+hipError_t launch_shader_clock(unsigned long long* out, unsigned long long ticks, hipStream_t s);
+
 hipError_t launch_attn_fwd_bf16(const FwdParams& p, hipStream_t s);
 hipError_t launch_attn_fwd_f32(const FwdParams& p, hipStream_t s);
 // Optional events (null = not recorded): before the dQ kernel, between it

@@ -27,7 +27,7 @@ EXPORTS = (
     "nc_attn_decode_workspace_bytes", "nc_attn_decode",
     "nc_attn_decode_step_workspace_bytes", "nc_attn_decode_step", "nc_kv_cache_replicate",
     "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd", "nc_attn_fwd_prologue",
-    "nc_profile_fwd_prologue",
+    "nc_profile_fwd_prologue", "nc_measure_shader_clock",
 )
 
 
@@ -64,6 +64,7 @@ _SIGS = {
     "nc_qk_prologue_fwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p], _i),
     "nc_attn_fwd_prologue": ([_i] * 6 + [_p] * 6 + [_i, _f, _i, _f] + [_p] * 4 + [_p], _i),
     "nc_qk_prologue_bwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p, _p, _p], _i),
+    "nc_measure_shader_clock": ([_p, _i, _p], _i),
 }
 
 
@@ -292,6 +293,16 @@ def nc_kv_cache_replicate(src, dst, n_tokens, stream=None):
                                      _stream(stream))
     _raise_on("nc_kv_cache_replicate", st)
     return dst
+
+
+def nc_measure_shader_clock(milliseconds, out=None, stream=None):
+    """Enqueue the clock probe on `stream` (a torch.cuda.Stream, default current); returns the int64
+    device tensor [2] it fills: shader cycles and 100 MHz ticks over `milliseconds` of wall time."""
+    import torch
+    if out is None:
+        out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    _raise_on("nc_measure_shader_clock", lib().nc_measure_shader_clock(_ptr(out), int(milliseconds), _stream(stream)))
+    return out
 
 
 def nc_rope_table(T_rope, D, base=100000.0, device="cuda", stream=None):
