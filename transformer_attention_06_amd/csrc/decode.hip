@@ -171,7 +171,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
 template <int D, int G, bool BF16>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
   constexpr int CHUNK = decode_chunk(D, G);
-  constexpr int MAXS = 64;  // chunks staged at once (T_max / CHUNK beyond this loops)
+  constexpr int MAXS = 32;  // chunks merged per batch (T_max / CHUNK beyond this loops)
   __shared__ float sm[MAXS], sl[MAXS];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
   const int L = p.seqlens[b];
@@ -188,13 +188,16 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
   const int lo = full ? 0 : L - p.window;
   const int s0 = lo / CHUNK, s1 = (L - 1) / CHUNK;
   const float* part = p.part + ((size_t)b * p.H + h) * p.n_split * (D + 2);
-  // The chunks' (m, l) are staged in LDS by one load per thread, so the
-  // merge does not wait for them one after another; each thread then sums
-  // its d over the chunks with independent loads.
+  // Per batch of up to MAXS chunks, each thread requests its element of
+  // every chunk's acc and (threads < nc) one chunk's (m, l) together: one
+  // memory round trip; the merge then runs out of registers and LDS.
   float M = -INFINITY, a = 0.f, z = 0.f;
   for (int c0 = s0; c0 <= s1; c0 += MAXS) {
     const int nc = min(MAXS, s1 - c0 + 1);
-    __syncthreads();
+    float av[MAXS];
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i) av[i] = i < nc ? part[(size_t)(c0 + i) * (D + 2) + t] : 0.f;
+    __syncthreads();  // the previous batch's (m, l) are no longer read
     if (t < nc) {
       sm[t] = part[(size_t)(c0 + t) * (D + 2) + D];
       sl[t] = part[(size_t)(c0 + t) * (D + 2) + D + 1];
@@ -207,12 +210,13 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
     a *= r;
     z *= r;
     M = Mn;
-#pragma unroll 8
-    for (int i = 0; i < nc; ++i) {
-      const float f = exp2_fast(sm[i] - M);
-      a = fmaf(f, part[(size_t)(c0 + i) * (D + 2) + t], a);
-      z = fmaf(f, sl[i], z);
-    }
+#pragma unroll
+    for (int i = 0; i < MAXS; ++i)
+      if (i < nc) {
+        const float f = exp2_fast(sm[i] - M);
+        a = fmaf(f, av[i], a);
+        z = fmaf(f, sl[i], z);
+      }
   }
   const float o = a / z;
   if (BF16)
