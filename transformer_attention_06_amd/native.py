@@ -364,7 +364,17 @@ def nc_qk_prologue_bwd(q, k, cos, sin, eps, dq_out, dk_out, pos_offset=None, dq=
 # autograd wrapper: saves out and lse, recomputes P in the backward kernel
 
 def attention(q, k, v, window, scale):
+    """Causal sliding-window GQA attention as a torch autograd op: q [B,T,H,D],
+    k/v [B,T,Hkv,D] (bf16 or float32, contiguous, on the GPU) -> out [B,T,H,D]."""
     return _Attention.apply(q, k, v, window, scale)
+
+
+def attention_qk_prologue(q, k, v, cos, sin, eps, window, scale, pos_offset=None):
+    """The training-side hot path as one autograd op: weightless RMSNorm and
+    half-split RoPE of the raw q, k (at positions pos_offset[b] + t), then
+    attention. The forward is nc_attn_fwd_prologue, the backward
+    nc_attn_bwd_prologue (gradients w.r.t. the raw q, k and v)."""
+    return _AttentionQK.apply(q, k, v, cos, sin, eps, window, scale, pos_offset)
 
 
 def _make_fn():
@@ -384,16 +394,35 @@ def _make_fn():
             dq, dk, dv = nc_attn_bwd(q, k, v, out, lse, dout.contiguous(), ctx.window, ctx.scale)
             return dq, dk, dv, None, None
 
-    return Attention
+    class AttentionQK(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, q, k, v, cos, sin, eps, window, scale, pos_offset):
+            qp, kp, out, lse = nc_attn_fwd_prologue(q, k, v, cos, sin, eps, window, scale, pos_offset=pos_offset)
+            ctx.save_for_backward(q, k, v, cos, sin, qp, kp, out, lse)
+            ctx.pos_offset, ctx.eps, ctx.window, ctx.scale = pos_offset, eps, window, scale
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, cos, sin, qp, kp, out, lse = ctx.saved_tensors
+            dq, dk, dv = nc_attn_bwd_prologue(qp, kp, v, out, lse, dout.contiguous(), ctx.window, ctx.scale, q, k,
+                                              cos, sin, ctx.eps, pos_offset=ctx.pos_offset)
+            return dq, dk, dv, None, None, None, None, None, None
+
+    return Attention, AttentionQK
 
 
 class _Lazy:
-    _fn = None
+    _fns = None
+
+    def __init__(self, i):
+        self.i = i
 
     def apply(self, *a):
-        if _Lazy._fn is None:
-            _Lazy._fn = _make_fn()
-        return _Lazy._fn.apply(*a)
+        if _Lazy._fns is None:
+            _Lazy._fns = _make_fn()
+        return _Lazy._fns[self.i].apply(*a)
 
 
-_Attention = _Lazy()
+_Attention = _Lazy(0)
+_AttentionQK = _Lazy(1)
