@@ -134,6 +134,9 @@ def main():
                      dtype=torch.uint8, device=dev)
     cos, sin = native.nc_rope_table(10 * T, D, 100000.0)
 
+    def wtag(w):
+        return "full" if w == FULL or w <= 0 else str(w)
+
     def step(tm=None):
         def ev(label):
             return tm.pair(label) if tm else (None, None)
@@ -148,6 +151,7 @@ def main():
                     x.record()  # materialise the events before handing them to the library
                 tm.add("prologue_fwd_k", e0, e1)
                 tm.add("attn_fwd", e1, e2)
+                tm.add("attn_fwd@" + wtag(wl.windows[l]), e1, e2)
                 native.nc_profile_fwd_prologue(e0, e1, e2)
             native.nc_attn_fwd_prologue(qr[l], kr[l], vv[l], cos, sin, eps, wl.windows[l], scale, q_out=qp[l],
                                         k_out=kp[l], out=out[l], lse=lse[l])
@@ -161,6 +165,9 @@ def main():
                     x.record()  # materialise the events before handing them to the library
                 tm.add("attn_bwd_dq", e0, e1)
                 tm.add("attn_bwd_dkdv", e1, e2)
+                tm.add("attn_bwd_dq@" + wtag(wl.windows[l]), e0, e1)
+                tm.add("attn_bwd_dkdv@" + wtag(wl.windows[l]), e1, e2)
+                tm.add("attn_bwd@" + wtag(wl.windows[l]), e0, e2)
                 native.nc_profile_bwd_main(e0, e1, e2)
             b and b.record()
             # attention backward and the prologue backward in one call: the
@@ -216,8 +223,18 @@ def main():
     # kernel 6*D (S and dP again, then dQ)
     kflops = {"attn_fwd": flops_f, "attn_bwd": flops_b, "attn_bwd_dkdv": flops_b,
               "attn_bwd_dq": attn_flops(B, T, H, D, wl.windows, "fwd") * 3 // 2}
-    kern = {}
+    kern, per_window = {}, {}
     for label, (ms, n) in tot.items():
+        if "@" in label:  # one layer type: per-launch time and its own band-counted rate
+            name, tag = label.split("@")
+            w = FULL if tag == "full" else int(tag)
+            f1 = attn_flops(B, T, H, D, [w], "fwd")
+            lf = {"attn_fwd": f1, "attn_bwd": 2 * f1, "attn_bwd_dkdv": 2 * f1, "attn_bwd_dq": f1 * 3 // 2}[name]
+            per_ms = ms / n
+            per_window.setdefault(tag, {})[name] = {
+                "avg_ms_per_launch": round(per_ms, 5), "tflops": round(lf / (per_ms * 1e-3) / 1e12, 2),
+                "frac_bf16_peak": round(lf / (per_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            continue
         per_step = ms / args.steps
         row = {"ms_per_step": round(per_step, 4), "launches_per_step": n // args.steps,
                "avg_ms_per_launch": round(ms / n, 5)}
@@ -373,6 +390,7 @@ def main():
                                   ((kern["attn_fwd"]["ms_per_step"] + kern["attn_bwd"]["ms_per_step"]) * 1e-3)
                                   / 1e12, 2),
         "kernels": kern,
+        "per_window": per_window,
         "decode": decode,
         "roofline": roofline,
         "cpu_baseline": cpu,
