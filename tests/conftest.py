@@ -23,7 +23,7 @@ def _gpu_available():
 
 @pytest.fixture(scope="session")
 def gpu():
-    """The loaded native library on a GPU machine; skips only where no GPU exists.
+    """The loaded native library on a machine with a GPU; skips only where no GPU exists.
 
     On a machine with a GPU a missing or unloadable library is an error, not
     a skip: the GPU tests must run the HIP path.

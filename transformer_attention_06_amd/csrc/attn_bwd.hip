@@ -180,8 +180,8 @@ __global__ __launch_bounds__(256) void bwd_pre_f32_kernel(BwdParams p) {
 // two workgroups per CU, 16x16x32 bf16 MFMA, 64-query steps. With 16 keys a
 // wave's stationary registers (K, V fragments and the dK, dV accumulators)
 // leave room for two waves of independent workgroups on every SIMD, which
-// hide each other's LDS and arithmetic latency (32 keys per wave on
-// 32x32x16 MFMA allowed one). Layouts (lane l,
+// hide each other's LDS and arithmetic latency (with 32 keys per wave on
+// 32x32x16 MFMA only one wave fits per SIMD). Layouts (lane l,
 // t = l % 16, g = l / 16): A operands hold A[t][8 g + e], B operands
 // B[8 g + e][t], results C[4 g + r][t].
 //   S = Q K^T per 16-query block: A = q rows (LDS), B = K^T (registers),
