@@ -16,7 +16,10 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,Hkv,D,T_max,w", [
     (8, 4, 4, 128, 300, 0), (8, 4, 4, 128, 300, 100), (5, 8, 2, 64, 700, 257),
-    (6, 6, 1, 32, 513, 0), (3, 8, 1, 128, 1024, 1), (4, 6, 2, 128, 256, 256)])
+    (6, 6, 1, 32, 513, 0), (3, 8, 1, 128, 1024, 1), (4, 6, 2, 128, 256, 256),
+    # more chunks per row than the combine merges in one batch (32): group 2
+    # with 40 chunks (full) and 34 (window 2100), group 8 with 64 chunks
+    (4, 4, 2, 128, 2500, 0), (4, 4, 2, 128, 2500, 2100), (3, 8, 1, 128, 1024, 0)])
 def test_decode_ragged_and_poisoned(gpu, dtype, B, H, Hkv, D, T_max, w):
     import torch
     from transformer_attention_06_amd import native

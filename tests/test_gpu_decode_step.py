@@ -25,7 +25,7 @@ def _lens(B, T_max, seed):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("B,H,Hkv,D,T_max,w", [
     (8, 4, 4, 128, 300, 0), (8, 4, 4, 128, 300, 100), (5, 8, 2, 64, 700, 257),
-    (6, 6, 1, 32, 513, 0), (3, 8, 1, 128, 1024, 1), (4, 6, 2, 128, 256, 256)])
+    (6, 6, 1, 32, 513, 0), (3, 8, 1, 128, 1024, 1), (4, 6, 2, 128, 256, 256), (4, 4, 2, 128, 2500, 0)])
 def test_decode_step_parity_and_cache_writes(gpu, dtype, B, H, Hkv, D, T_max, w):
     import torch
     from transformer_attention_06_amd import native
