@@ -21,6 +21,9 @@ Sources (titles and sections of the pages this follows):
     in-place cache update, batch-1 prefill replicated to the sample rows).
   * "nanochat (Fucina port)", "Architecture": no-weight RMSNorm, half-split
     RoPE built from an inverse-frequency table, grouped causal attention.
+  * "nanochat Admin & Developer Guide", section 5 "Precision: Explicit dtype
+    & FP8" (float8 e4m3 operands with tensorwise dynamic scaling) for the
+    fp8 forward in fp8.py.
 
 Parity pins for every function live in tests/test_oracle.py (closed forms,
 invariants, brute force, finite differences and torch fp64 library
@@ -50,4 +53,13 @@ from .engine import (  # noqa: F401
     kv_cache_replicate,
     cache_append,
     prefill_chunk,
+)
+from .fp8 import (  # noqa: F401
+    E4M3_MAX,
+    e4m3_value,
+    e4m3_decode,
+    e4m3_encode,
+    tensorwise_descale,
+    quantize_tensorwise,
+    attn_fwd_fp8,
 )

@@ -6,9 +6,14 @@ from transformer_attention_06_amd import synth
 
 # Tolerances: float32 configurations max-abs <= 1e-4; bfloat16 rel-L2 <= 5e-3
 # on out and <= 1e-2 on dq/dk/dv; lse max-abs <= 1e-3 (bf16) / 1e-4 (f32).
+# fp8 (e4m3 operands, bf16 out): the kernel rounds P to e4m3 (3 mantissa
+# bits, relative rounding error up to 2^-4) before P V; emulating that in
+# fp64 gives out rel-L2 ~ 0.019 on N(0,1) operands, so out <= 4e-2; lse
+# comes from float32 statistics as in the bf16 path.
 TOL = {
     "f32": dict(out=("maxabs", 1e-4), lse=("maxabs", 1e-4), grad=("maxabs", 1e-4)),
     "bf16": dict(out=("rel_l2", 5e-3), lse=("maxabs", 1e-3), grad=("rel_l2", 1e-2)),
+    "fp8": dict(out=("rel_l2", 4e-2), lse=("maxabs", 1e-3)),
 }
 
 
