@@ -88,6 +88,25 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
                       void* out, float* lse, nc_stream stream);
 
 /*
+ * Attention forward of fp8 operands ("nanochat Admin & Developer Guide",
+ * section 5 "Precision: Explicit dtype & FP8": forward operands in float8
+ * e4m3 with tensorwise scaling; section 6: the attention kernel accepts fp8
+ * as well as bf16). q, k, v are float8 e4m3 codes in the OCP "fn" encoding
+ * (1 byte per element, no infinities), each tensor with one descale: the
+ * operands are q = value(q8) * q_descale, likewise k, v. Computes the
+ * forward of nc_attn_fwd on those values:
+ *   q8 [B,T,H,D], k8/v8 [B,T,Hkv,D] (bytes) -> out [B,T,H,D] bf16, lse [B,H,T] f32
+ * Products on the 32x32x64 fp8 matrix cores with float32 accumulation,
+ * softmax statistics in float32; the probabilities are rounded to e4m3
+ * (round to nearest even) before the P.V product. D in {64, 128}
+ * (NC_ERR_UNSUPPORTED otherwise); scale and the descales must be finite and
+ * > 0, NC_ERR_INVALID_ARG otherwise. Pointers 16-byte aligned.
+ */
+nc_status nc_attn_fwd_fp8(int B, int T, int H, int Hkv, int D, const void* q8, const void* k8,
+                          const void* v8, float q_descale, float k_descale, float v_descale,
+                          int window, float scale, void* out, float* lse, nc_stream stream);
+
+/*
  * A chunk of Tq queries per row against a KV cache: the SDPA fallback's
  * chunked-inference case ("nanochat Admin & Developer Guide", section 6: the
  * queries are fewer than the keys and the visible keys are a shifted causal,

@@ -169,6 +169,19 @@ def test_profile_hook_validation(L):
     assert L.nc_profile_bwd_main(None, None, None) == OK
 
 
+def test_fp8_forward_validation(L):
+    f = L.nc_attn_fwd_fp8
+    assert f(1, 16, 2, 1, 32, A, A, A, 1.0, 1.0, 1.0, 0, 0.1, A, A, None) == UNSUPPORTED  # D = 32
+    assert "D=32" in msg(L)
+    assert f(1, 16, 2, 1, 128, A, A, A, 0.0, 1.0, 1.0, 0, 0.1, A, A, None) == INVALID  # descale 0
+    assert f(1, 16, 2, 1, 128, A, A, A, 1.0, float("nan"), 1.0, 0, 0.1, A, A, None) == INVALID
+    assert f(1, 16, 2, 1, 128, A, A, A, 1.0, 1.0, float("inf"), 0, 0.1, A, A, None) == INVALID
+    assert "descale" in msg(L)
+    assert f(1, 16, 2, 1, 128, None, A, A, 1.0, 1.0, 1.0, 0, 0.1, A, A, None) == INVALID
+    assert f(1, 16, 3, 2, 128, A, A, A, 1.0, 1.0, 1.0, 0, 0.1, A, A, None) == INVALID  # H % Hkv
+    assert f(1, 16, 2, 1, 128, A, A, A, 1e30, 1e30, 1.0, 0, 0.1, A, A, None) == INVALID  # scale overflow
+
+
 def test_clock_probe_validation(L):
     assert L.nc_measure_shader_clock(None, 10, None) == INVALID
     assert "out" in msg(L)

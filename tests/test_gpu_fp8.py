@@ -1,0 +1,99 @@
+"""GPU parity of the fp8 (e4m3) attention forward against the fp64 oracle,
+through the C ABI. Operands are drawn N(0, 1), quantized on the device by
+torch's float8_e4m3fn cast with the tensorwise descale amax / 448 (the
+oracle's own encoder matches that cast code for code), and the oracle
+evaluates the attention of the dequantized codes."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import check, f64, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def quantize(x):
+    """x (device tensor) -> (e4m3 codes on the device, descale as a float)."""
+    import torch
+    s = float(x.abs().max()) / 448.0
+    return (x / s).to(torch.float8_e4m3fn), s
+
+
+def codes_np(x8):
+    import torch
+    return x8.view(torch.uint8).cpu().numpy()
+
+
+CASES = [
+    (1, 64, 2, 1, 128, 0), (2, 127, 4, 4, 64, 64), (1, 129, 4, 1, 128, 1), (1, 257, 8, 2, 128, 127),
+    (1, 300, 2, 2, 64, 129), (2, 333, 6, 2, 128, 200), (1, 256, 2, 1, 128, 256), (2, 130, 8, 8, 128, 65),
+    (1, 1100, 2, 1, 128, 0), (1, 1100, 2, 1, 128, 500), (1, 513, 16, 2, 128, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "B{}T{}H{}Hkv{}D{}w{}".format(*c))
+def test_fp8_forward_parity(gpu, case):
+    from transformer_attention_06_amd import native
+    B, T, H, Hkv, D, w = case
+    print("case", case, flush=True)
+    scale = 1.0 / math.sqrt(D)
+    q, k, v = inputs([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D)], 600, "f32")
+    (q8, sq), (k8, sk), (v8, sv) = quantize(q), quantize(k), quantize(v)
+    out, lse = native.nc_attn_fwd_fp8(q8, k8, v8, sq, sk, sv, w, scale)
+    ro, rl = oracle.attn_fwd_fp8(codes_np(q8), codes_np(k8), codes_np(v8), sq, sk, sv, w, scale)
+    check(f"fp8 out {case}", f64(out), ro, "fp8", "out")
+    check(f"fp8 lse {case}", f64(lse), rl, "fp8", "lse")
+
+
+def test_fp8_descales(gpu):
+    """v's descale multiplies out exactly; q's and k's act through the
+    logit scale only."""
+    import torch
+    from transformer_attention_06_amd import native
+    B, T, H, Hkv, D, w = 1, 200, 4, 2, 128, 77
+    q, k, v = inputs([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D)], 610, "f32")
+    (q8, sq), (k8, sk), (v8, sv) = quantize(q), quantize(k), quantize(v)
+    o1, l1 = native.nc_attn_fwd_fp8(q8, k8, v8, sq, sk, sv, w, 0.1)
+    o2, l2 = native.nc_attn_fwd_fp8(q8, k8, v8, sq, sk, 2 * sv, w, 0.1)
+    o3, l3 = native.nc_attn_fwd_fp8(q8, k8, v8, 4 * sq, sk, sv, w, 0.025)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, 2 * o1) and torch.equal(l2, l1)
+    assert torch.equal(o3, o1) and torch.equal(l3, l1)
+
+
+def test_fp8_one_key_window_returns_v(gpu):
+    import torch
+    from transformer_attention_06_amd import native
+    B, T, H, Hkv, D = 2, 150, 4, 2, 64
+    q, k, v = inputs([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D)], 620, "f32")
+    (q8, sq), (k8, sk), (v8, sv) = quantize(q), quantize(k), quantize(v)
+    out, _ = native.nc_attn_fwd_fp8(q8, k8, v8, sq, sk, sv, 1, 0.125)
+    torch.cuda.synchronize()
+    vd = oracle.e4m3_decode(codes_np(v8)) * sv
+    want = np.repeat(vd, H // Hkv, axis=2)
+    # P = 1 exactly, so out is the dequantized v rounded once to bf16
+    got = f64(out)
+    assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -8)
+
+
+def test_fp8_d20_sampled_rows(gpu):
+    """The d20 shape (B=32, T=2048, H=Hkv=10, D=128) on one windowed and one
+    full layer, checked on two batch rows the oracle computes."""
+    import torch
+    from transformer_attention_06_amd import native, synth
+    B, T, H, D = 32, 2048, 10, 128
+    scale = 1.0 / math.sqrt(D)
+    for w in (1024, 0):
+        q, k, v = (synth.normal_device((B, T, H, D), 630 + i + (0 if w else 10), "bf16") for i in range(3))
+        (q8, sq), (k8, sk), (v8, sv) = quantize(q.float()), quantize(k.float()), quantize(v.float())
+        out, lse = native.nc_attn_fwd_fp8(q8, k8, v8, sq, sk, sv, w, scale)
+        torch.cuda.synchronize()
+        for b in (0, 31):
+            print("d20 fp8 row", b, "window", w, flush=True)
+            ro, rl = oracle.attn_fwd_fp8(codes_np(q8[b:b + 1]), codes_np(k8[b:b + 1]), codes_np(v8[b:b + 1]),
+                                         sq, sk, sv, w, scale)
+            check(f"d20 fp8 out row {b} w{w}", f64(out[b:b + 1]), ro, "fp8", "out")
+            check(f"d20 fp8 lse row {b} w{w}", f64(lse[b:b + 1]), rl, "fp8", "lse")

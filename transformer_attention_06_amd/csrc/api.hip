@@ -150,6 +150,29 @@ nc_status nc_attn_fwd(nc_dtype dt, int B, int T, int H, int Hkv, int D, const vo
   return finish(dt == NC_BF16 ? nc::launch_attn_fwd_bf16(p, s) : nc::launch_attn_fwd_f32(p, s), s, "nc_attn_fwd");
 }
 
+nc_status nc_attn_fwd_fp8(int B, int T, int H, int Hkv, int D, const void* q, const void* k, const void* v,
+                          float q_descale, float k_descale, float v_descale, int window, float scale, void* out,
+                          float* lse, nc_stream stream) {
+  NC_TRY(check_shape(NC_BF16, B, T, H, Hkv, D));
+  if (D != 64 && D != 128) return fail(NC_ERR_UNSUPPORTED, "fp8 forward: head dim D=%d not in {64, 128}", D);
+  NC_TRY(check_ptr(q, "q"));
+  NC_TRY(check_ptr(k, "k"));
+  NC_TRY(check_ptr(v, "v"));
+  NC_TRY(check_ptr(out, "out"));
+  NC_TRY(check_ptr(lse, "lse"));
+  NC_TRY(check_scale(scale));
+  const float ds[3] = {q_descale, k_descale, v_descale};
+  for (float d : ds)
+    if (!(d > 0.f) || !isfinite(d)) return fail(NC_ERR_INVALID_ARG, "descales must be finite and > 0");
+  const double sl2 = (double)scale * q_descale * k_descale * 1.4426950408889634;
+  if (!(sl2 > 0.0) || !isfinite((float)sl2))
+    return fail(NC_ERR_INVALID_ARG, "scale * q_descale * k_descale is not a finite float");
+  NC_TRY(check_device(nullptr));
+  nc::Fp8FwdParams p{q, k, v, out, lse, B, T, H, Hkv, D, norm_window(window, T), (float)sl2, v_descale};
+  hipStream_t s = (hipStream_t)stream;
+  return finish(nc::launch_attn_fwd_fp8(p, s), s, "nc_attn_fwd_fp8");
+}
+
 nc_status nc_attn_fwd_cache(nc_dtype dt, int B, int Tq, int H, int Hkv, int D, int T_max, const void* q,
                             const void* k_cache, const void* v_cache, const int32_t* cache_seqlens, int window,
                             float scale, void* out, float* lse, nc_stream stream) {

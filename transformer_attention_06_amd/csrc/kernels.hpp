@@ -115,6 +115,20 @@ struct AppendParams {
 constexpr int decode_keys_per_group(int G) { return G <= 2 ? 16 : (G <= 4 ? 8 : 4); }
 constexpr int decode_chunk(int D, int G) { return (64 / (D / 8)) * decode_keys_per_group(G); }
 
+// Forward of float8 e4m3 operands (one descale per tensor), bf16 out.
+struct Fp8FwdParams {
+  const void* q;  // e4m3 codes [B, T, H, D]
+  const void* k;  // [B, T, Hkv, D]
+  const void* v;
+  void* out;      // bf16 [B, T, H, D]
+  float* lse;     // [B, H, T], natural log of the scaled scores
+  int B, T, H, Hkv, D;
+  int window;        // 0 = full causal, otherwise 1 <= window < T
+  float scale_log2;  // scale * q_descale * k_descale * log2(e)
+  float v_descale;
+};
+hipError_t launch_attn_fwd_fp8(const Fp8FwdParams& p, hipStream_t s);
+
 // Average shader clock: out[0] shader cycles and out[1] 100 MHz ticks over
 // `ticks` ticks of wall time (device memory, 2 values).
 hipError_t launch_shader_clock(unsigned long long* out, unsigned long long ticks, hipStream_t s);

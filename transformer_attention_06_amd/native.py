@@ -27,7 +27,7 @@ EXPORTS = (
     "nc_attn_decode_workspace_bytes", "nc_attn_decode",
     "nc_attn_decode_step_workspace_bytes", "nc_attn_decode_step", "nc_kv_cache_replicate",
     "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd", "nc_attn_fwd_prologue",
-    "nc_profile_fwd_prologue", "nc_measure_shader_clock",
+    "nc_profile_fwd_prologue", "nc_measure_shader_clock", "nc_attn_fwd_fp8",
 )
 
 
@@ -65,6 +65,7 @@ _SIGS = {
     "nc_attn_fwd_prologue": ([_i] * 6 + [_p] * 6 + [_i, _f, _i, _f] + [_p] * 4 + [_p], _i),
     "nc_qk_prologue_bwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p, _p, _p], _i),
     "nc_measure_shader_clock": ([_p, _i, _p], _i),
+    "nc_attn_fwd_fp8": ([_i] * 5 + [_p] * 3 + [_f] * 3 + [_i, _f, _p, _p, _p], _i),
 }
 
 
@@ -136,6 +137,21 @@ def nc_attn_fwd(q, k, v, window, scale, out=None, lse=None, stream=None):
     st = lib().nc_attn_fwd(_dt(q), B, T, H, Hkv, D, _ptr(q), _ptr(k), _ptr(v), int(window),
                            float(scale), _ptr(out), _ptr(lse), _stream(stream))
     _raise_on("nc_attn_fwd", st)
+    return out, lse
+
+
+def nc_attn_fwd_fp8(q8, k8, v8, q_descale, k_descale, v_descale, window, scale, out=None, lse=None,
+                    stream=None):
+    """float8 e4m3 q8 [B,T,H,D], k8/v8 [B,T,Hkv,D] (torch.float8_e4m3fn or uint8 codes) with one
+    descale per tensor -> (out [B,T,H,D] bf16, lse [B,H,T] float32)."""
+    import torch
+    B, T, H, D = q8.shape
+    Hkv = k8.shape[2]
+    out = torch.empty((B, T, H, D), dtype=torch.bfloat16, device=q8.device) if out is None else out
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=q8.device) if lse is None else lse
+    st = lib().nc_attn_fwd_fp8(B, T, H, Hkv, D, _ptr(q8), _ptr(k8), _ptr(v8), float(q_descale), float(k_descale),
+                               float(v_descale), int(window), float(scale), _ptr(out), _ptr(lse), _stream(stream))
+    _raise_on("nc_attn_fwd_fp8", st)
     return out, lse
 
 
