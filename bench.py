@@ -31,6 +31,7 @@ import time
 
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 NOMINAL_SCLK_MHZ = 2400.0  # the shader clock that peak is quoted at
+PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "attn fwd+bwd TFLOP/s (band-counted) at d20 T=2048; decode GB/s"
 
@@ -69,6 +70,7 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     return ap.parse_args()
 
 
@@ -350,6 +352,39 @@ def main():
         log("prefill chunk:", json.dumps(decode["prefill_chunk"]))
         del kc, vc, cq_
 
+    # ------------------------------------------------------- fp8 forward
+    fp8 = None
+    if not args.no_fp8:
+        # the d20 operands quantized to e4m3 with one descale per tensor
+        # (outside the timed region), then the 20-layer forward
+        def q8(x):
+            s8 = float(x.abs().max()) / 448.0
+            return (x.float() / s8).to(torch.float8_e4m3fn), s8
+        f8 = [(q8(qr[l]), q8(kr[l]), q8(vv[l])) for l in range(L)]
+        f8o = torch.empty_like(qr[0])
+        f8l = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+
+        def fp8_step():
+            for l in range(L):
+                (a, sa), (b_, sb), (c, sc) = f8[l]
+                native.nc_attn_fwd_fp8(a, b_, c, sa, sb, sc, wl.windows[l], scale, out=f8o, lse=f8l)
+
+        for _ in range(args.warmup):
+            fp8_step()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(args.steps):
+            fp8_step()
+        t1.record()
+        torch.cuda.synchronize()
+        fms = t0.elapsed_time(t1) / args.steps
+        fp8 = {"what": "nc_attn_fwd_fp8 per layer on the d20 operands quantized to float8 e4m3 (one descale per "
+                       "tensor), 20-layer SSSL windows; bf16 out",
+               "ms_per_step": round(fms, 4), "tflops": round(flops_f / (fms * 1e-3) / 1e12, 2),
+               "frac_fp8_peak": round(flops_f / (fms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
+        log("fp8 forward:", json.dumps(fp8))
+        del f8
+
     # ------------------------------------------------------------- roofline
     dom = max(("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"), key=lambda k: kern[k]["ms_per_step"])
     dom_flops = kflops[dom]
@@ -392,6 +427,7 @@ def main():
         "kernels": kern,
         "per_window": per_window,
         "decode": decode,
+        "fp8_forward": fp8,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
