@@ -56,7 +56,7 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const void* lds_addr) {
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
 template <int D>
-__global__ __launch_bounds__(F8_THREADS, 2) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
+__global__ __launch_bounds__(F8_THREADS, 3) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
   constexpr int NC = D / 16;              // 16-byte chunks per row (one byte per element)
   constexpr int KS = D / 64;              // 64-wide steps of d in S
   constexpr int ND = D / 32;              // 32-row blocks of d in O^T
