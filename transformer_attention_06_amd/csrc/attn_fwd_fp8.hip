@@ -55,6 +55,15 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const void* lds_addr) {
 // LDS row r of a V tile holds key swap23(r) (bits 2 and 3 exchanged).
 __device__ __forceinline__ int swap23(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 
+// Chunk permutation of the V tile (chunk c of row r at c ^ swz_v(r)): the
+// 32 lanes of a transpose read cover 8 consecutive rows x an aligned pair of
+// chunks; the xor moves each row's pair to its own 32-byte bank slot (K
+// tiles keep swz, which suits their 16-row operand reads).
+template <int NC>
+__device__ __forceinline__ int swz_v(int r) {
+  return NC >= 8 ? ((r >> 1) & 3) << 1 : ((r >> 2) & 1) << 1;
+}
+
 template <int D>
 __global__ __launch_bounds__(F8_THREADS, 3) void attn_fwd_fp8_kernel(Fp8FwdParams p) {
   constexpr int NC = D / 16;              // 16-byte chunks per row (one byte per element)
@@ -101,18 +110,19 @@ __global__ __launch_bounds__(F8_THREADS, 3) void attn_fwd_fp8_kernel(Fp8FwdParam
 
   // Tile copies: lane l of instruction n writes LDS row (inst * RPI + l / NC),
   // physical chunk l % NC, holding logical chunk (l % NC) ^ swz(row) of its
-  // source row: the same row for K, key swap23(row) for V. Rows past the keys
+  // source row (swz_v for V): the same row for K, key swap23(row) for V. Rows past the keys
   // present are clamped to T - 1 (finite, masked for every valid query).
   unsigned ld_k[IPW], ld_v[IPW];
-  int ld_rk[IPW], ld_rv[IPW], ld_ch[IPW];
+  int ld_rk[IPW], ld_rv[IPW], ld_ck[IPW], ld_cv[IPW];
 #pragma unroll
   for (int n = 0; n < IPW; ++n) {
     const int row = (wave * IPW + n) * RPI + lane / NC;
     ld_rk[n] = row;
     ld_rv[n] = swap23(row);
-    ld_ch[n] = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
-    ld_k[n] = (unsigned)(ld_rk[n] * kvrs + ld_ch[n] * 16);
-    ld_v[n] = (unsigned)(ld_rv[n] * kvrs + ld_ch[n] * 16);
+    ld_ck[n] = (lane % NC) ^ (swz<NC>(row) & (NC - 1));
+    ld_cv[n] = (lane % NC) ^ (swz_v<NC>(row) & (NC - 1));
+    ld_k[n] = (unsigned)(ld_rk[n] * kvrs + ld_ck[n] * 16);
+    ld_v[n] = (unsigned)(ld_rv[n] * kvrs + ld_cv[n] * 16);
   }
   auto issue_tile = [&](int jt, int buf) {
     const int j0 = jt * F8_BN;
@@ -126,8 +136,8 @@ __global__ __launch_bounds__(F8_THREADS, 3) void attn_fwd_fp8_kernel(Fp8FwdParam
     } else {
 #pragma unroll
       for (int n = 0; n < IPW; ++n) {
-        const unsigned ok = (unsigned)(min(j0 + ld_rk[n], T - 1) * kvrs + ld_ch[n] * 16);
-        const unsigned ov = (unsigned)(min(j0 + ld_rv[n], T - 1) * kvrs + ld_ch[n] * 16);
+        const unsigned ok = (unsigned)(min(j0 + ld_rk[n], T - 1) * kvrs + ld_ck[n] * 16);
+        const unsigned ov = (unsigned)(min(j0 + ld_rv[n], T - 1) * kvrs + ld_cv[n] * 16);
         dma16(krs, ok, 0u, lds_u32(&kv_lds[buf][0][(wave * IPW + n) * RPI * D]));
         dma16(vrs, ov, 0u, lds_u32(&kv_lds[buf][1][(wave * IPW + n) * RPI * D]));
       }
@@ -153,7 +163,7 @@ __global__ __launch_bounds__(F8_THREADS, 3) void attn_fwd_fp8_kernel(Fp8FwdParam
     for (int qq = 0; qq < 4; ++qq) {
       const int row = 16 * qq + 8 * hh + (t16 >> 1);
       const int lc = 2 * db + (li >> 4);
-      voff[db][qq] = row * D + ((lc ^ (swz<NC>(row) & (NC - 1))) << 4) + 8 * (t16 & 1);
+      voff[db][qq] = row * D + ((lc ^ (swz_v<NC>(row) & (NC - 1))) << 4) + 8 * (t16 & 1);
     }
 
   int qw = 0, qi = 0;
