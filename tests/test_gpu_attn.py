@@ -125,3 +125,13 @@ def test_bf16_long_and_wide_groups(gpu, case):
     from transformer_attention_06_amd import native
     print("case", case, flush=True)
     run_case(native, *case, "bf16", seed=300)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("T,w", [(1, 0), (2, 0), (2, 1), (3, 2), (17, 0), (17, 5)])
+def test_short_sequences(gpu, dtype, T, w):
+    """Sequences shorter than one tile: a single token (out = v, the only key
+    is the query's own), two and three tokens, one partial tile."""
+    from transformer_attention_06_amd import native
+    print("short case", T, w, dtype, flush=True)
+    run_case(native, 2, T, 4, 2, 64, w, dtype, seed=230 + T)

@@ -97,3 +97,16 @@ def test_fp8_d20_sampled_rows(gpu):
                                          sq, sk, sv, w, scale)
             check(f"d20 fp8 out row {b} w{w}", f64(out[b:b + 1]), ro, "fp8", "out")
             check(f"d20 fp8 lse row {b} w{w}", f64(lse[b:b + 1]), rl, "fp8", "lse")
+
+
+@pytest.mark.parametrize("T,w", [(1, 0), (2, 0), (3, 2), (17, 5)])
+def test_fp8_short_sequences(gpu, T, w):
+    from transformer_attention_06_amd import native
+    print("fp8 short case", T, w, flush=True)
+    B, H, Hkv, D = 2, 4, 2, 128
+    q, k, v = inputs([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D)], 640 + T, "f32")
+    (q8, sq), (k8, sk), (v8, sv) = quantize(q), quantize(k), quantize(v)
+    out, lse = native.nc_attn_fwd_fp8(q8, k8, v8, sq, sk, sv, w, 0.125)
+    ro, rl = oracle.attn_fwd_fp8(codes_np(q8), codes_np(k8), codes_np(v8), sq, sk, sv, w, 0.125)
+    check(f"fp8 short out T{T}", f64(out), ro, "fp8", "out")
+    check(f"fp8 short lse T{T}", f64(lse), rl, "fp8", "lse")
