@@ -34,7 +34,10 @@
  * last error. Requirements checked: non-null pointers, sizes >= 1,
  * H % Hkv == 0, D in {32, 64, 128}, a known dtype, 16-byte aligned tensor
  * pointers, element counts below 2^31, sufficient workspace, and a gfx950
- * current device (NC_ERR_DEVICE otherwise). A launch failure reported by the
+ * current device (NC_ERR_DEVICE otherwise). Grid limits (NC_ERR_UNSUPPORTED):
+ * the float32 attention path takes B, H <= 65535; decode takes B <= 65535
+ * and at most 65535 cache chunks (T_max <= 65535 * chunk, the chunk being
+ * 64 positions at D = 128 for groups of 1 or 2 heads). A launch failure reported by the
  * runtime gives NC_ERR_LAUNCH; outputs are then undefined. Outputs must not
  * alias inputs. All entry points are thread-safe and reentrant.
  */

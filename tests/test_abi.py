@@ -182,6 +182,18 @@ def test_fp8_forward_validation(L):
     assert f(1, 16, 2, 1, 128, A, A, A, 1e30, 1e30, 1.0, 0, 0.1, A, A, None) == INVALID  # scale overflow
 
 
+def test_grid_limits(L):
+    # float32 attention: heads and rows on the second and third grid axes
+    assert fwd(L, dt=F32, B=70000, T=1, H=1, Hkv=1, D=32) == UNSUPPORTED
+    assert "65535" in msg(L)
+    assert fwd(L, dt=F32, B=1, T=1, H=70000, Hkv=1, D=32) == UNSUPPORTED
+    # decode: rows and cache chunks (64 positions per chunk at D = 128, group 1)
+    d = L.nc_attn_decode
+    assert d(BF16, 70000, 1, 1, 128, 1, A, A, A, A, 0, 0.1, A, A, A, 1 << 40, None) == UNSUPPORTED
+    assert d(BF16, 1, 1, 1, 128, 65535 * 64 + 1, A, A, A, A, 0, 0.1, A, A, A, 1 << 40, None) == UNSUPPORTED
+    assert "T_max" in msg(L)
+
+
 def test_clock_probe_validation(L):
     assert L.nc_measure_shader_clock(None, 10, None) == INVALID
     assert "out" in msg(L)

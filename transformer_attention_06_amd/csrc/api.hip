@@ -33,6 +33,7 @@ nc_status fail(nc_status s, const char* fmt, ...) {
 }
 
 constexpr long long kMaxElems = 2147483647LL;  // per-tensor element count limit (int32 indexing margin)
+constexpr int kMaxGridYZ = 65535;              // largest second / third grid dimension
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -45,6 +46,19 @@ nc_status check_shape(nc_dtype dt, int B, int T, int H, int Hkv, int D) {
   if (D != 32 && D != 64 && D != 128) return fail(NC_ERR_UNSUPPORTED, "head dim D=%d not in {32, 64, 128}", D);
   if ((long long)B * T * H * D > kMaxElems)
     return fail(NC_ERR_UNSUPPORTED, "tensor of B*T*H*D=%lld elements exceeds 2^31-1", (long long)B * T * H * D);
+  // the float32 kernels put heads and rows on the second and third grid axes
+  if (dt == NC_F32 && (B > kMaxGridYZ || H > kMaxGridYZ))
+    return fail(NC_ERR_UNSUPPORTED, "float32 path: B=%d and H=%d must be <= %d", B, H, kMaxGridYZ);
+  return NC_OK;
+}
+
+// Decode grids: rows on the third axis, chunks of the cache on the second.
+nc_status check_decode_grid(int B, int T_max, int D, int G) {
+  if (B > kMaxGridYZ) return fail(NC_ERR_UNSUPPORTED, "decode: B=%d exceeds %d rows", B, kMaxGridYZ);
+  const int chunk = nc::decode_chunk(D, G);
+  if ((T_max + chunk - 1) / chunk > kMaxGridYZ)
+    return fail(NC_ERR_UNSUPPORTED, "decode: T_max=%d exceeds %lld positions at D=%d", T_max,
+                (long long)kMaxGridYZ * chunk, D);
   return NC_OK;
 }
 
@@ -318,6 +332,7 @@ nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, c
     return fail(NC_ERR_UNSUPPORTED, "cache of B*T_max*Hkv*D elements exceeds 2^31-1");
   if (!nc::decode_group_supported(H / Hkv))
     return fail(NC_ERR_UNSUPPORTED, "decode supports query groups H/Hkv in {1,2,3,4,6,8}, got %d", H / Hkv);
+  NC_TRY(check_decode_grid(B, T_max, D, H / Hkv));
   NC_TRY(check_ptr(q, "q"));
   NC_TRY(check_ptr(k_cache, "k_cache"));
   NC_TRY(check_ptr(v_cache, "v_cache"));
@@ -356,6 +371,7 @@ nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_m
     return fail(NC_ERR_UNSUPPORTED, "cache of B*T_max*Hkv*D elements exceeds 2^31-1");
   if (!nc::decode_group_supported(H / Hkv))
     return fail(NC_ERR_UNSUPPORTED, "decode supports query groups H/Hkv in {1,2,3,4,6,8}, got %d", H / Hkv);
+  NC_TRY(check_decode_grid(B, T_max, D, H / Hkv));
   NC_TRY(check_ptr(q, "q"));
   NC_TRY(check_ptr(k_new, "k_new"));
   NC_TRY(check_ptr(v_new, "v_new"));
