@@ -194,10 +194,25 @@ def main():
         marks[i + 1].record()
     torch.cuda.synchronize()
     ms_step = marks[0].elapsed_time(marks[-1]) / args.steps
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)  # for the phases below
     per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
     spread = {q: round(float(np.percentile(per_step, pc)), 4) for q, pc in (("p10", 10), ("median", 50), ("p90", 90))}
     log(f"timed {args.steps} steps: {ms_step:.3f} ms/step, per step {json.dumps(spread)}")
+
+    def time_phase(fn):
+        """Warmup, then args.steps repetitions of fn with an event after each:
+        (mean ms per repetition, p10/median/p90 of the repetitions)."""
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev[0].record()
+        for i in range(args.steps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        reps = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps))
+        return (ev[0].elapsed_time(ev[-1]) / args.steps,
+                {q: round(float(np.percentile(reps, pc)), 4) for q, pc in (("p10", 10), ("median", 50), ("p90", 90))})
     # The shader clock while the same steps run again: a one-wave probe on a
     # second stream that reads the shader-cycle and 100 MHz counters.
     side = torch.cuda.Stream()
@@ -270,20 +285,12 @@ def main():
                 native.nc_attn_decode(dq_[l], kc[l], vc[l], sl, w, dw.scale, out=dout_, lse=dlse,
                                       workspace=dws)
 
-        for _ in range(args.warmup):
-            dstep()
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(args.steps):
-            dstep()
-        t1.record()
-        torch.cuda.synchronize()
-        dms = t0.elapsed_time(t1) / args.steps
+        dms, dms_spread = time_phase(dstep)
         nbytes = sum(decode_bytes(lens, DH, DHkv, DD, w) for w in dw.windows)
         gbs = nbytes / (dms * 1e-3) / 1e9
         decode = {"workload": "decode_bf16: 64 rows x 1 query, H=Hkv=10, D=128, cache lengths "
                               "uniform 1..2048, 20-layer SSSL step (15 x w=1024, 5 full)",
-                  "ms_per_step": round(dms, 4), "bytes_per_step": nbytes, "gbs": round(gbs, 1),
+                  "ms_per_step": round(dms, 4), "ms_per_step_spread": dms_spread, "bytes_per_step": nbytes, "gbs": round(gbs, 1),
                   "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
         log("decode:", json.dumps(decode))
 
@@ -301,21 +308,13 @@ def main():
                 native.nc_attn_decode_step(dq_[l], kn_[l], vn_[l], kc[l], vc[l], csl, dcos, dsin, eps, w,
                                            dw.scale, out=dout_, lse=dlse, workspace=sws)
 
-        for _ in range(args.warmup):
-            sstep()
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(args.steps):
-            sstep()
-        t1.record()
-        torch.cuda.synchronize()
-        sms = t0.elapsed_time(t1) / args.steps
+        sms, sms_spread = time_phase(sstep)
         sbytes = sum(decode_step_bytes(lens - 1, DH, DHkv, DD, w) for w in dw.windows)
         sgbs = sbytes / (sms * 1e-3) / 1e9
         decode["step_with_append"] = {
             "what": "nc_attn_decode_step per layer: prologue of the new token at position "
                     "cache_seqlens[b] = L_b - 1, k'/v appended in place, split-K decode over L_b keys",
-            "ms_per_step": round(sms, 4), "bytes_per_step": sbytes, "gbs": round(sgbs, 1),
+            "ms_per_step": round(sms, 4), "ms_per_step_spread": sms_spread, "bytes_per_step": sbytes, "gbs": round(sgbs, 1),
             "frac_hbm_peak": round(sgbs / PEAK_HBM_GBS, 4)}
         log("decode step:", json.dumps(decode["step_with_append"]))
 
@@ -333,21 +332,13 @@ def main():
             for l, w in enumerate(dw.windows):
                 native.nc_attn_fwd_cache(cq_[l], kc[l], vc[l], coff_d, w, dw.scale, out=cout, lse=clse)
 
-        for _ in range(args.warmup):
-            cstep()
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(args.steps):
-            cstep()
-        t1.record()
-        torch.cuda.synchronize()
-        cms = t0.elapsed_time(t1) / args.steps
+        cms, cms_spread = time_phase(cstep)
         cflops = sum(4 * DD * DH * chunk_pairs(int(n0), CQ, w) for w in dw.windows for n0 in coff)
         ctf = cflops / (cms * 1e-3) / 1e12
         decode["prefill_chunk"] = {
             "what": "nc_attn_fwd_cache per layer: 64 rows x 512-token chunk at offsets uniform 0..1536 "
                     "against the [64, 2048, 10, 128] caches, 20-layer SSSL windows",
-            "ms_per_step": round(cms, 4), "band_flops": cflops, "tflops": round(ctf, 2),
+            "ms_per_step": round(cms, 4), "ms_per_step_spread": cms_spread, "band_flops": cflops, "tflops": round(ctf, 2),
             "frac_bf16_peak": round(ctf / PEAK_BF16_TFLOPS, 4)}
         log("prefill chunk:", json.dumps(decode["prefill_chunk"]))
         del kc, vc, cq_
@@ -369,18 +360,10 @@ def main():
                 (a, sa), (b_, sb), (c, sc) = f8[l]
                 native.nc_attn_fwd_fp8(a, b_, c, sa, sb, sc, wl.windows[l], scale, out=f8o, lse=f8l)
 
-        for _ in range(args.warmup):
-            fp8_step()
-        torch.cuda.synchronize()
-        t0.record()
-        for _ in range(args.steps):
-            fp8_step()
-        t1.record()
-        torch.cuda.synchronize()
-        fms = t0.elapsed_time(t1) / args.steps
+        fms, fms_spread = time_phase(fp8_step)
         fp8 = {"what": "nc_attn_fwd_fp8 per layer on the d20 operands quantized to float8 e4m3 (one descale per "
                        "tensor), 20-layer SSSL windows; bf16 out",
-               "ms_per_step": round(fms, 4), "tflops": round(flops_f / (fms * 1e-3) / 1e12, 2),
+               "ms_per_step": round(fms, 4), "ms_per_step_spread": fms_spread, "tflops": round(flops_f / (fms * 1e-3) / 1e12, 2),
                "frac_fp8_peak": round(flops_f / (fms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)}
         log("fp8 forward:", json.dumps(fp8))
         del f8
