@@ -1,0 +1,79 @@
+"""Seeded random shapes through the whole path, against the fp64 oracle:
+the fused prologue + forward, the backward through attention and prologue,
+decode over random cache lengths, and (bf16, D 64/128) the fp8 forward.
+Each case draws D, the group size, Hkv, B, T (1..699), the window (0, 1, 2,
+random, T, beyond T), the dtype, the scale and per-row position offsets, so
+the suite reaches tile tails, degenerate windows and group layouts that the
+enumerated cases do not list."""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.parity import check, f64, inputs
+
+pytestmark = pytest.mark.gpu
+
+EPS = 2.0 ** -23
+
+
+def _case(seed):
+    rng = np.random.default_rng(seed)
+    D = int(rng.choice([32, 64, 128]))
+    G = int(rng.choice([1, 2, 3, 4, 6, 8]))
+    Hkv = int(rng.integers(1, 3))
+    B = int(rng.integers(1, 4))
+    T = int(rng.integers(1, 700))
+    w = int(rng.choice([0, 1, 2, int(rng.integers(1, T + 2)), T, T + 5]))
+    dtype = "bf16" if rng.random() < 0.75 else "f32"
+    scale = float(rng.choice([1.0, 1.44])) / math.sqrt(D)
+    pos = rng.integers(0, 50, B).astype(np.int32)
+    lens = rng.integers(1, T + 1, B).astype(np.int32)
+    return dict(B=B, T=T, H=G * Hkv, Hkv=Hkv, D=D, w=w, dtype=dtype, scale=scale, pos=pos, lens=lens,
+                seed=int(rng.integers(0, 10 ** 6)))
+
+
+@pytest.mark.parametrize("seed", range(900, 924))
+def test_random_shape(gpu, seed):
+    import torch
+    from transformer_attention_06_amd import native
+    c = _case(seed)
+    B, T, H, Hkv, D, w, dtype, scale = (c[n] for n in ("B", "T", "H", "Hkv", "D", "w", "dtype", "scale"))
+    tag = f"seed {seed}: B{B} T{T} H{H} Hkv{Hkv} D{D} w{w} {dtype} scale {scale:.4f}"
+    print(tag, flush=True)
+    q, k, v, do = inputs([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D), (B, T, H, D)], c["seed"], dtype)
+    cos, sin = native.nc_rope_table(T + 60, D)
+    posd = torch.from_numpy(c["pos"]).cuda()
+    qp, kp, out, lse = native.nc_attn_fwd_prologue(q, k, v, cos, sin, EPS, w, scale, pos_offset=posd)
+    dq, dk, dv = native.nc_attn_bwd_prologue(qp, kp, v, out, lse, do, w, scale, q, k, cos, sin, EPS, pos_offset=posd)
+    positions = oracle.positions_from_offsets(B, T, c["pos"])
+    rq, rk = oracle.qk_prologue_fwd(f64(q), f64(k), positions, EPS)
+    check(tag + " q'", f64(qp), rq, dtype, "out")
+    check(tag + " k'", f64(kp), rk, dtype, "out")
+    # attention and its backward read q', k' as stored in the dtype
+    ro, rl = oracle.attn_fwd(f64(qp), f64(kp), f64(v), w, scale)
+    check(tag + " out", f64(out), ro, dtype, "out")
+    check(tag + " lse", f64(lse), rl, dtype, "lse")
+    gq, gk, gv = oracle.attn_bwd(f64(qp), f64(kp), f64(v), f64(do), w, scale)
+    rdq, rdk = oracle.qk_prologue_bwd(f64(q), f64(k), positions, gq, gk, EPS)
+    check(tag + " dq", f64(dq), rdq, dtype, "grad")
+    check(tag + " dk", f64(dk), rdk, dtype, "grad")
+    check(tag + " dv", f64(dv), gv, dtype, "grad")
+    # decode: one query per row against k', v taken as a cache of T slots
+    qd = q[:, 0].contiguous()
+    od, ld = native.nc_attn_decode(qd, kp, v, torch.from_numpy(c["lens"]).cuda(), w, scale)
+    rod, rld = oracle.decode(f64(qd), f64(kp), f64(v), c["lens"], w, scale)
+    check(tag + " decode out", f64(od), rod, dtype, "out")
+    check(tag + " decode lse", f64(ld), rld, dtype, "lse")
+    if dtype == "bf16" and D in (64, 128):
+        def quant(x):
+            s = float(x.abs().max()) / 448.0
+            return (x / s).to(torch.float8_e4m3fn), s
+        (q8, sq), (k8, sk), (v8, sv) = quant(q.float()), quant(k.float()), quant(v.float())
+        o8, l8 = native.nc_attn_fwd_fp8(q8, k8, v8, sq, sk, sv, w, scale)
+        codes = lambda t: t.view(torch.uint8).cpu().numpy()  # noqa: E731
+        r8, rl8 = oracle.attn_fwd_fp8(codes(q8), codes(k8), codes(v8), sq, sk, sv, w, scale)
+        check(tag + " fp8 out", f64(o8), r8, "fp8", "out")
+        check(tag + " fp8 lse", f64(l8), rl8, "fp8", "lse")
