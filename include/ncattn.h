@@ -245,8 +245,8 @@ nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max,
  *   -> out [B,H,D], lse [B,H]
  * k' is stored in the cache's dtype and the attention reads that stored
  * value; q' is kept in float32. The inputs must not overlap the caches. The
- * workspace (size from nc_attn_decode_step_workspace_bytes) holds the
- * split-K partials, q' and the row key counts.
+ * workspace (size from nc_attn_decode_step_workspace_bytes, the same as
+ * nc_attn_decode's) holds the split-K partials.
  */
 size_t nc_attn_decode_step_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, int D, int T_max);
 nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_max,

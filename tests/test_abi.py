@@ -236,11 +236,9 @@ def test_bwd_prologue_validation(L):
 
 
 def test_decode_step_workspace_query_is_pure(L):
-    pad = lambda n: -(-n // 256) * 256  # noqa: E731
-    for dt in (BF16, F32):  # partials, q' (float32 whatever the dtype), row lengths
-        parts = L.nc_attn_decode_workspace_bytes(dt, 64, 10, 10, 128, 2048)
+    for dt in (BF16, F32):  # the split-K partials, as for nc_attn_decode
         assert L.nc_attn_decode_step_workspace_bytes(dt, 64, 10, 10, 128, 2048) == \
-            pad(parts) + pad(64 * 10 * 128 * 4) + pad(64 * 4)
+            L.nc_attn_decode_workspace_bytes(dt, 64, 10, 10, 128, 2048) == 64 * 10 * 32 * 130 * 4
     assert L.nc_attn_decode_step_workspace_bytes(BF16, 3, 4, 3, 32, 257) == 0
 
 

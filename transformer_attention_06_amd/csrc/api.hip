@@ -353,12 +353,9 @@ nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, c
   return finish(nc::launch_decode(p, dt == NC_BF16, s), s, "nc_attn_decode");
 }
 
-static size_t pad256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 size_t nc_attn_decode_step_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, int D, int T_max) {
-  const size_t parts = nc_attn_decode_workspace_bytes(dt, B, H, Hkv, D, T_max);
-  if (parts == 0) return 0;
-  return pad256(parts) + pad256((size_t)B * H * D * 4) + pad256((size_t)B * 4);  // partials, q' (f32), lengths
+  return nc_attn_decode_workspace_bytes(dt, B, H, Hkv, D, T_max);  // the split-K partials only
 }
 
 nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q,
@@ -391,20 +388,12 @@ nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_m
   if (!workspace || !aligned16(workspace) || workspace_bytes < need)
     return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   NC_TRY(check_device(nullptr));
-  char* ws = (char*)workspace;
-  float* parts = (float*)ws;
-  void* q_prime = ws + pad256(nc_attn_decode_workspace_bytes(dt, B, H, Hkv, D, T_max));
-  int32_t* lens = (int32_t*)((char*)q_prime + pad256((size_t)B * H * D * 4));
+  // the split kernel applies the prologue and writes the cache slot itself
+  nc::DecodeParams p{q, k_cache, v_cache, cache_seqlens, out, lse, (float*)workspace, B, H, Hkv, D, T_max,
+                     window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), 0, scale,
+                     scale * 1.4426950408889634f, 1, k_new, v_new, cos_tab, sin_tab, T_rope, eps};
   hipStream_t s = (hipStream_t)stream;
-  nc::AppendParams ap{q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos_tab, sin_tab, q_prime, lens,
-                      B, H, Hkv, D, T_max, T_rope, eps};
-  hipError_t e = nc::launch_decode_append(ap, dt == NC_BF16, s);
-  if (e == hipSuccess) {
-    nc::DecodeParams p{q_prime, k_cache, v_cache, lens, out, lse, parts, B, H, Hkv, D, T_max,
-                       window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), 1, scale,
-                       scale * 1.4426950408889634f};
-    e = nc::launch_decode(p, dt == NC_BF16, s);
-  }
+  const hipError_t e = nc::launch_decode(p, dt == NC_BF16, s);
   return finish(e, s, "nc_attn_decode_step");
 }
 

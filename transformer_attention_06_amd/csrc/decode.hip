@@ -21,6 +21,14 @@
 //   Chunks outside a row's key range exit without reading anything.
 // decode_combine: merges a row's partials into out and lse. A length outside
 //   1..T_max yields NaN out and lse for that row.
+// Decode step (the in-place cache update of FA3's kvcache call that the
+//   pages describe: section 7, per-row int32 cache_seqlens): row b holds
+//   n = cache_seqlens[b] cached tokens and the new token sits at position n.
+//   The split kernel applies the forward prologue at position n to the raw
+//   q (kept in float32) and to the raw new key; the wave whose chunk holds
+//   position n uses the new k' (rounded to the cache dtype) and v for that
+//   position and writes both into cache slot n. A row whose n is outside
+//   0 .. min(T_max, T_rope) - 1 writes nothing and gets NaN out and lse.
 // replicate: copies a batch-1 prompt cache row into every decode row (section
 //   7: the prompt is prefilled once and its cache copied to the samples).
 // cache_append: writes a chunk's k and v into the cache slots that follow
@@ -32,6 +40,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "rope.hpp"
 
 namespace nc {
 namespace {
@@ -67,6 +76,36 @@ __device__ __forceinline__ void unpack_raw8(const Raw8<BF16>& r, float* f) {
   }
 }
 
+// Keys row b attends to (its query sits at position keys - 1); a value
+// outside 1..T_max marks the row invalid.
+__device__ __forceinline__ int row_keys(const DecodeParams& p, int b) {
+  const int n = p.seqlens[b];
+  if (!p.step) return n;
+  return (n >= 0 && n < p.T_max && n < p.T_rope) ? n + 1 : 0;
+}
+
+template <bool BF16>
+__device__ __forceinline__ Raw8<BF16> to_raw8(const float* f) {
+  Raw8<BF16> r;
+  if (BF16) {
+    r.w[0] = pack8_bf16(f);
+  } else {
+    r.w[0] = __builtin_bit_cast(u32x4, (f32x4){f[0], f[1], f[2], f[3]});
+    r.w[BF16 ? 0 : 1] = __builtin_bit_cast(u32x4, (f32x4){f[4], f[5], f[6], f[7]});
+  }
+  return r;
+}
+template <bool BF16>
+__device__ __forceinline__ void store_raw8(const void* base, size_t elem_off, const Raw8<BF16>& r) {
+  if (BF16) {
+    *(u32x4*)((unsigned short*)const_cast<void*>(base) + elem_off) = r.w[0];
+  } else {
+    u32x4* d = (u32x4*)((float*)const_cast<void*>(base) + elem_off);
+    d[0] = r.w[0];
+    d[1] = r.w[BF16 ? 0 : 1];
+  }
+}
+
 template <int D, int G, bool BF16>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   constexpr int LPR = D / 8;              // lanes per cache row (divides 16)
@@ -76,7 +115,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
   static_assert(CHUNK == decode_chunk(D, G), "chunk size mismatch");
 
   const int g = blockIdx.x, sp = blockIdx.y, b = blockIdx.z;
-  const int L = p.seqlens[b];
+  const int L = row_keys(p, b);
   if (L < 1 || L > p.T_max) return;
   const bool full = p.window <= 0 || p.window >= L;
   const int lo = full ? 0 : L - p.window;
@@ -108,12 +147,40 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     }
   }
 
+  // decode step: in the wave whose chunk holds position n, the new token's
+  // k' and v (every group computes the same vector, all lanes active for the
+  // group exchanges) replace what the cache slot held and are written there
+  float cs[8], sn[8];
+  if (p.step) load_angles8<D>(p.cos_tab, p.sin_tab, L - 1, c, cs, sn);
+  if (p.step && sp == (L - 1) / CHUNK) {
+    const int n = L - 1;
+    float x[8], kp[8];
+    ld8<BF16>(p.k_new, ((size_t)b * p.Hkv + g) * D + c * 8, x);
+    prologue8<D>(x, cs, sn, c, p.eps, kp);
+    const Raw8<BF16> knew = to_raw8<BF16>(kp);
+    const Raw8<BF16> vnew = load_raw8<BF16>(p.v_new, ((size_t)b * p.Hkv + g) * D + c * 8);
+#pragma unroll
+    for (int u = 0; u < KPG; ++u)
+      if (j0 + NGR * u == n) {
+        kr[u] = knew;
+        vr[u] = vnew;
+      }
+    if (grp == 0) {
+      store_raw8<BF16>(p.k_cache, cache_base + (size_t)n * rs, knew);
+      store_raw8<BF16>(p.v_cache, cache_base + (size_t)n * rs, vnew);
+    }
+  }
+
 #pragma unroll
   for (int hq = 0; hq < G; ++hq) {
     float qf[8];
     {
       float t[8];
-      if (BF16 && !p.q_f32)
+      if (p.step) {  // raw q in the cache dtype: the prologue at position n, kept in float32
+        float x[8];
+        ld8<BF16>(p.q, ((size_t)b * H + g * G + hq) * D + c * 8, x);
+        prologue8<D>(x, cs, sn, c, p.eps, t);
+      } else if (BF16 && !p.q_f32)
         unpack8_bf16(*(const u32x4*)((const unsigned short*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8), t);
       else {
         const f32x4* pq = (const f32x4*)((const float*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8);
@@ -174,7 +241,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeParams p) {
   constexpr int MAXS = 32;  // chunks merged per batch (T_max / CHUNK beyond this loops)
   __shared__ float sm[MAXS], sl[MAXS];
   const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
-  const int L = p.seqlens[b];
+  const int L = row_keys(p, b);
   const size_t oi = ((size_t)b * p.H + h) * D + t;
   if (L < 1 || L > p.T_max) {
     if (BF16)

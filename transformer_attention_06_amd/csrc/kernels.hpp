@@ -75,6 +75,17 @@ struct DecodeParams {
   int q_f32;  // q is float32 whatever the cache dtype
   float scale;
   float scale_log2;
+  // Decode step (step != 0): q [B,H,D], k_new, v_new [B,Hkv,D] are raw, in
+  // the cache dtype; seqlens[b] counts the tokens already cached (the new
+  // one goes to slot n = seqlens[b] and the row attends to n + 1 keys). The
+  // kernels apply the prologue at position n and write k', v into the slot.
+  int step;
+  const void* k_new;
+  const void* v_new;
+  const float* cos_tab;  // [T_rope, D/2]
+  const float* sin_tab;
+  int T_rope;
+  float eps;
 };
 
 struct PrologueParams {
@@ -88,24 +99,6 @@ struct PrologueParams {
   void* q_out;         // forward: q'; backward: dq
   void* k_out;         // forward: k'; backward: dk
   int B, T, H, Hkv, D, T_rope;
-  float eps;
-};
-
-// Decode step: forward prologue of the new token at position cache_seqlens[b],
-// its k' and v written into the cache there, q' and the key counts for the
-// decode kernels written to q_out and seqlens_out.
-struct AppendParams {
-  const void* q;      // [B, H, D] raw
-  const void* k_new;  // [B, Hkv, D] raw
-  const void* v_new;  // [B, Hkv, D]
-  void* k_cache;      // [B, T_max, Hkv, D]
-  void* v_cache;
-  const int32_t* cache_seqlens;  // [B] tokens already cached
-  const float* cos_tab;          // [T_rope, D/2]
-  const float* sin_tab;
-  void* q_out;           // [B, H, D] float32
-  int32_t* seqlens_out;  // [B] keys per row including the new token (0: row invalid)
-  int B, H, Hkv, D, T_max, T_rope;
   float eps;
 };
 
@@ -143,7 +136,6 @@ struct BwdEvents {
 hipError_t launch_attn_bwd_bf16(const BwdParams& p, hipStream_t s, const BwdEvents& ev);
 hipError_t launch_attn_bwd_f32(const BwdParams& p, hipStream_t s, const BwdEvents& ev);
 hipError_t launch_decode(const DecodeParams& p, bool bf16, hipStream_t s);
-hipError_t launch_decode_append(const AppendParams& p, bool bf16, hipStream_t s);
 // Chunk k/v [B, Tq, Hkv, D] into cache slots cache_seqlens[b] .. + Tq - 1 (rows
 // whose slots do not fit are left alone).
 hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
