@@ -347,7 +347,7 @@ nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, c
     return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
   NC_TRY(check_device(nullptr));
   nc::DecodeParams p{q, k_cache, v_cache, seqlens, out, lse, (float*)workspace, B, H, Hkv, D, T_max,
-                     window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), 0, scale,
+                     window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), scale,
                      scale * 1.4426950408889634f};
   hipStream_t s = (hipStream_t)stream;
   return finish(nc::launch_decode(p, dt == NC_BF16, s), s, "nc_attn_decode");
@@ -390,7 +390,7 @@ nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_m
   NC_TRY(check_device(nullptr));
   // the split kernel applies the prologue and writes the cache slot itself
   nc::DecodeParams p{q, k_cache, v_cache, cache_seqlens, out, lse, (float*)workspace, B, H, Hkv, D, T_max,
-                     window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), 0, scale,
+                     window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), scale,
                      scale * 1.4426950408889634f, 1, k_new, v_new, cos_tab, sin_tab, T_rope, eps};
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = nc::launch_decode(p, dt == NC_BF16, s);

@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
         float x[8];
         ld8<BF16>(p.q, ((size_t)b * H + g * G + hq) * D + c * 8, x);
         prologue8<D>(x, cs, sn, c, p.eps, t);
-      } else if (BF16 && !p.q_f32)
+      } else if (BF16)
         unpack8_bf16(*(const u32x4*)((const unsigned short*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8), t);
       else {
         const f32x4* pq = (const f32x4*)((const float*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8);

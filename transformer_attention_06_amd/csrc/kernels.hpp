@@ -72,7 +72,6 @@ struct DecodeParams {
   int B, H, Hkv, D, T_max;
   int window;  // <= 0 full
   int n_split;
-  int q_f32;  // q is float32 whatever the cache dtype
   float scale;
   float scale_log2;
   // Decode step (step != 0): q [B,H,D], k_new, v_new [B,Hkv,D] are raw, in
