@@ -155,11 +155,29 @@ nc_status nc_kv_cache_append(nc_dtype dt, int B, int Tq, int Hkv, int D, int T_m
  *   dv_j = sum_{h in group} sum_i P_ij dout_i.
  * dk/dv are summed over the query heads of each group. dq/dk/dv are fully
  * overwritten. q, k, v, out, lse must be those of nc_attn_fwd with the same
- * window and scale. The float32 workspace holds delta [B,H,T] and
- * lse*log2(e) [B,H,T]; its size is nc_attn_bwd_workspace_bytes().
- * dq, dk and dv are deterministic (no atomics; dq comes from its own
- * query-stationary pass).
+ * window and scale.
+ * Defined by the attention call it differentiates ("nanochat Admin &
+ * Developer Guide", section 6 "Attention: FA3 with SDPA Fallback": causal
+ * GQA with the layer's window; section 3: the sliding-window schedule) and
+ * by the pages' statement that upstream takes this gradient with autograd
+ * ("nanochat (Python)" catalog, "Model & kernels"): the formulas above are
+ * the chain rule through the softmax, loss convention L = sum(out * dout).
+ * bf16: products on bf16 matrix cores with float32 accumulation, P and dS
+ * rounded to bf16 before the products that consume them, gradients rounded
+ * to nearest even. f32: float32 throughout.
+ *   q, out, dout [B,T,H,D], k, v [B,T,Hkv,D] (dt), lse [B,H,T] (f32)
+ *   -> dq [B,T,H,D], dk, dv [B,T,Hkv,D] (dt)
+ * workspace: caller-owned DEVICE memory of at least
+ * nc_attn_bwd_workspace_bytes() bytes, 16-byte aligned; it holds float32
+ * delta [B,H,T] and lse*log2(e) [B,H,T] (each padded to 256 bytes), is
+ * fully overwritten, and carries nothing between calls (NC_ERR_WORKSPACE if
+ * NULL or smaller). Calls that share a workspace must be ordered on one
+ * stream. dq, dk and dv are deterministic (no atomics; dq comes from its own
+ * query-stationary pass). Errors as in the header comment.
  */
+/* Bytes of workspace nc_attn_bwd and nc_attn_bwd_prologue need for these
+ * sizes (section 6's attention call and its backward, as above); a pure
+ * function of its arguments, 0 for invalid sizes. */
 size_t nc_attn_bwd_workspace_bytes(nc_dtype dt, int B, int T, int H, int Hkv, int D);
 nc_status nc_attn_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
                       const void* q, const void* k, const void* v,
@@ -244,7 +262,9 @@ nc_status nc_attn_decode(nc_dtype dt, int B, int H, int Hkv, int D, int T_max,
  *   k_cache/v_cache [B,T_max,Hkv,D] (read and written), cos/sin [T_rope,D/2]
  *   -> out [B,H,D], lse [B,H]
  * k' is stored in the cache's dtype and the attention reads that stored
- * value; q' is kept in float32. The inputs must not overlap the caches. The
+ * value; q' is rounded to that dtype too, as the prologue's output is in the
+ * forward (nc_attn_fwd_prologue), so the step attends like the last row of a
+ * prefill of the same tokens. The inputs must not overlap the caches. The
  * workspace (size from nc_attn_decode_step_workspace_bytes, the same as
  * nc_attn_decode's) holds the split-K partials.
  */
@@ -340,6 +360,20 @@ nc_status nc_measure_shader_clock(unsigned long long* out, int milliseconds, nc_
  * QK prologue backward: given dq_out, dk_out (gradients w.r.t. the prologue
  * outputs) and the raw q, k, writes dq, dk w.r.t. the raw inputs:
  *   u = R(-theta) dy,  r = sqrt(mean x^2 + eps),  dx = u / r - x <x, u> / (D r^3).
+ * It differentiates nc_qk_prologue_fwd ("nanochat Admin & Developer Guide",
+ * section 3: weightless QK RMSNorm then half-split RoPE with base 100000,
+ * applied to q and k right before attention; the pages take this gradient
+ * with autograd, "nanochat (Python)" catalog, "Model & kernels"): the
+ * transpose of the rotation by theta = p * base^(-2d/D), then the
+ * transposed Jacobian of the norm, d(x_i/r)/dx_k = delta_ik/r - x_i x_k/(D r^3).
+ * Positions p = (pos_offset ? pos_offset[b] : 0) + t as in the forward
+ * (pos_offset a DEVICE int32 array [B] or NULL); a position outside
+ * 0..T_rope-1 writes NaN for that vector. Statistics in float32, results
+ * rounded to the dtype.
+ *   q, dq_out [B,T,H,D], k, dk_out [B,T,Hkv,D] (raw inputs and incoming
+ *   gradients, dtype dt), cos/sin [T_rope,D/2] f32
+ *   -> dq [B,T,H,D], dk [B,T,Hkv,D] (dt)
+ * Outputs must not alias inputs. Errors as in the header comment.
  */
 nc_status nc_qk_prologue_bwd(nc_dtype dt, int B, int T, int H, int Hkv, int D,
                              const void* q, const void* k, const int32_t* pos_offset,

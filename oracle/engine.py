@@ -16,7 +16,11 @@ product path.
     The cache is storage of the model's dtype, so what the attention reads
     back from slot n is k' as stored in that dtype: with cache_dtype "bf16"
     (or "f32") the appended k' and v are rounded to it before the attention,
-    like every other cache entry; cache_dtype None keeps them exact.
+    like every other cache entry; cache_dtype None keeps them exact. q' is
+    an activation of the model's dtype too (the prologue's outputs enter the
+    attention as tensors of that dtype, section 3), so it is rounded to
+    cache_dtype as well: the step then attends exactly as the last row of a
+    prefill whose prologue outputs are stored in that dtype.
   * Cache replication. Section 7 "KV cache" and "Generation flow": the
     prompt is prefilled once with batch 1 and that cache is copied to every
     sample row. Only the prompt's positions are copied.
@@ -75,6 +79,7 @@ def decode_step(q, k_new, v_new, k_cache, v_cache, cache_seqlens, window, scale,
         raise ValueError("cache_seqlens must be [B] with values in 0..T_max-1")
     pos = n[:, None]  # [B, 1]: the new token's position
     qp, kp = qk_prologue_fwd(q[:, None], k_new[:, None], pos, eps, base)
+    qp = round_to(qp, cache_dtype)
     for b in range(B):
         kc[b, n[b]] = round_to(kp[b, 0], cache_dtype)
         vc[b, n[b]] = round_to(v_new[b], cache_dtype)

@@ -346,6 +346,10 @@ def test_round_to_matches_torch_casts():
 
 
 def test_decode_step_stores_the_appended_key_in_the_cache_dtype():
+    # the cache holds the model's dtype and q' is an activation of that dtype
+    # ("nanochat Admin & Developer Guide", section 3: the prologue's outputs
+    # enter attention as model tensors; section 7 "KV cache": the cache is
+    # written in place and read back as stored)
     B, T_max, H, Hkv, D, eps = 2, 6, 2, 1, 8, 1e-6
     q, k, v = rnd((B, H, D), 78), rnd((B, Hkv, D), 79), rnd((B, Hkv, D), 80)
     kc, vc = rnd((B, T_max, Hkv, D), 81), rnd((B, T_max, Hkv, D), 82)
@@ -355,9 +359,10 @@ def test_decode_step_stores_the_appended_key_in_the_cache_dtype():
     for b in range(B):
         np.testing.assert_array_equal(k2[b, n[b]], oracle.round_to(k1[b, n[b]], "bf16"))
         np.testing.assert_array_equal(v2[b, n[b]], oracle.round_to(v[b], "bf16"))
-    # the attention reads the stored values: same as a decode over the rounded cache
-    o3, l3 = oracle.decode(oracle.qk_prologue_fwd(q[:, None], k[:, None], n[:, None], eps)[0][:, 0], k2, v2, n + 1,
-                           0, 0.3)
+    # the attention reads the stored values with q' rounded to the same dtype:
+    # the same as a decode of the rounded q' over the rounded cache
+    qr = oracle.round_to(oracle.qk_prologue_fwd(q[:, None], k[:, None], n[:, None], eps)[0][:, 0], "bf16")
+    o3, l3 = oracle.decode(qr, k2, v2, n + 1, 0, 0.3)
     np.testing.assert_allclose(o2, o3, rtol=0, atol=1e-15)
     np.testing.assert_allclose(l2, l3, rtol=0, atol=1e-15)
     assert np.abs(o2 - o1).max() > 0
@@ -458,6 +463,49 @@ def test_rope_position_zero_is_identity_and_d2_is_plane_rotation():
     y = oracle.rope_rotate(e1, pos)
     np.testing.assert_allclose(y[0, :, 0, 0], np.cos(np.arange(5)), rtol=0, atol=1e-15)
     np.testing.assert_allclose(y[0, :, 0, 1], np.sin(np.arange(5)), rtol=0, atol=1e-15)
+
+
+def test_position_offsets_are_absolute_positions():
+    # positions_from_offsets with non-zero offsets ("nanochat Admin & Developer
+    # Guide", section 7 "KV cache": each row's position comes from its int32
+    # cache_seqlens entry). Pinned three ways, none of which re-types the
+    # oracle's formula:
+    #   (a) D = 2: a unit vector at token t of row b is rotated by exactly
+    #       o_b + t radians, checked against the complex exponential;
+    #   (b) a row with offset o is the slice o .. o + T - 1 of the same row
+    #       prologued from position 0 (a dropped, doubled or sign-flipped
+    #       offset, or an off-by-one, fails);
+    #   (c) the decode step at n applies the prologue at position n, i.e. the
+    #       offset form with T = 1.
+    offs = np.array([0, 7, 1000, 3])
+    B, T = len(offs), 5
+    pos = oracle.positions_from_offsets(B, T, offs)
+    assert pos.shape == (B, T)
+    e1 = np.zeros((B, T, 1, 2))
+    e1[..., 0] = 1.0
+    y = oracle.rope_rotate(e1, pos)
+    for b, o in enumerate(offs):
+        z = np.exp(1j * (o + np.arange(T)))
+        np.testing.assert_allclose(y[b, :, 0, 0], z.real, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(y[b, :, 0, 1], z.imag, rtol=0, atol=1e-12)
+    D, eps = 16, 2.0 ** -23
+    q, k = rnd((B, T, 3, D), 480), rnd((B, T, 1, D), 481)
+    qa, ka = oracle.qk_prologue_fwd(q, k, pos, eps)
+    for b, o in enumerate(offs):
+        qq = np.concatenate([rnd((1, o, 3, D), 482), q[b:b + 1]], axis=1)
+        kk = np.concatenate([rnd((1, o, 1, D), 483), k[b:b + 1]], axis=1)
+        qz, kz = oracle.qk_prologue_fwd(qq, kk, oracle.positions_from_offsets(1, o + T), eps)
+        np.testing.assert_allclose(qa[b], qz[0, o:], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(ka[b], kz[0, o:], rtol=0, atol=1e-13)
+    assert np.abs(qa[1] - oracle.qk_prologue_fwd(q[1:2], k[1:2], oracle.positions_from_offsets(1, T), eps)[0][0]
+                  ).max() > 1e-2
+    n = np.array([0, 9, 3])
+    qd, kd, vd = rnd((3, 2, D), 484), rnd((3, 1, D), 485), rnd((3, 1, D), 486)
+    kc = rnd((3, 12, 1, D), 487)
+    _, _, kc2, _ = oracle.decode_step(qd, kd, vd, kc, kc.copy(), n, 0, 0.3, eps)
+    _, kw = oracle.qk_prologue_fwd(qd[:, None], kd[:, None], oracle.positions_from_offsets(3, 1, n), eps)
+    for b in range(3):
+        np.testing.assert_allclose(kc2[b, n[b]], kw[b, 0], rtol=0, atol=1e-15)
 
 
 def test_rope_preserves_norm_and_is_relative():

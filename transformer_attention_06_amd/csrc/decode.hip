@@ -25,7 +25,8 @@
 //   pages describe: section 7, per-row int32 cache_seqlens): row b holds
 //   n = cache_seqlens[b] cached tokens and the new token sits at position n.
 //   The split kernel applies the forward prologue at position n to the raw
-//   q (kept in float32) and to the raw new key; the wave whose chunk holds
+//   q and to the raw new key, both rounded to the cache dtype as the
+//   prologue's outputs are in the forward; the wave whose chunk holds
 //   position n uses the new k' (rounded to the cache dtype) and v for that
 //   position and writes both into cache slot n. A row whose n is outside
 //   0 .. min(T_max, T_rope) - 1 writes nothing and gets NaN out and lse.
@@ -176,10 +177,11 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeParams p) {
     float qf[8];
     {
       float t[8];
-      if (p.step) {  // raw q in the cache dtype: the prologue at position n, kept in float32
+      if (p.step) {  // raw q in the cache dtype: the prologue at position n, q' rounded to that dtype
         float x[8];
         ld8<BF16>(p.q, ((size_t)b * H + g * G + hq) * D + c * 8, x);
         prologue8<D>(x, cs, sn, c, p.eps, t);
+        if (BF16) unpack8_bf16(pack8_bf16(t), t);
       } else if (BF16)
         unpack8_bf16(*(const u32x4*)((const unsigned short*)p.q + ((size_t)b * H + g * G + hq) * D + c * 8), t);
       else {
