@@ -112,8 +112,8 @@ def test_decode_steps_reproduce_prefill(gpu, w):
     T = P + S
     pos = oracle.positions_from_offsets(B, T)
     rq, rk = oracle.qk_prologue_fwd(f64(qs), f64(ks), pos, EPS)
-    # every key is read back from the bf16 cache
-    ro, rl = oracle.attn_fwd(rq, oracle.round_to(rk, "bf16"), f64(vs), w, scale)
+    # q' and every key are activations of the model dtype (keys read back from the bf16 cache)
+    ro, rl = oracle.attn_fwd(oracle.round_to(rq, "bf16"), oracle.round_to(rk, "bf16"), f64(vs), w, scale)
     check("last step out", f64(out), ro[:, T - 1], "bf16", "out")
     check("last step lse", f64(lse), rl[:, :, T - 1], "bf16", "lse")
     check("cache k'", f64(kc[:, :T]), rk, "bf16", "out")
@@ -132,3 +132,72 @@ def test_kv_cache_replicate(gpu, dtype):
     for r in range(n_rows):
         assert torch.equal(dst[r, :n_tok], src[:n_tok])
     assert (dst[:, n_tok:] == -7.0).all()
+
+
+@pytest.mark.parametrize("w", [0, 256])
+def test_decode_step_equals_last_row_of_the_fused_prefill(gpu, w):
+    # The library's two paths over the same tokens: nc_attn_fwd_prologue over
+    # the raw sequence (positions 0..T-1) and nc_attn_decode_step for the last
+    # token against a cache holding the forward's own k' for slots 0..T-2.
+    # Both round q' and k' to bf16 and attend with float32 statistics; they
+    # differ only in P (bf16 before the P V product in the forward, float32
+    # in the decode), so they are held to the oracle parity bars: out rel-L2
+    # <= 5e-3, lse max-abs <= 1e-3.
+    import torch
+    from transformer_attention_06_amd import native
+    B, T, H, Hkv, D = 3, 700, 4, 2, 128
+    scale = 1.0 / math.sqrt(D)
+    print("fused prefill vs decode step, window", w, flush=True)
+    q, k, v = inputs([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D)], 440, "bf16")
+    c, s = native.nc_rope_table(T, D)
+    qp, kp, out, lse = native.nc_attn_fwd_prologue(q, k, v, c, s, EPS, w, scale)
+    kc = torch.full((B, T, Hkv, D), float("nan"), dtype=q.dtype, device="cuda")
+    vc = torch.full_like(kc, float("nan"))
+    kc[:, :T - 1] = kp[:, :T - 1]
+    vc[:, :T - 1] = v[:, :T - 1]
+    n = torch.full((B,), T - 1, dtype=torch.int32, device="cuda")
+    od, ld = native.nc_attn_decode_step(q[:, T - 1].contiguous(), k[:, T - 1].contiguous(), v[:, T - 1].contiguous(),
+                                        kc, vc, n, c, s, EPS, w, scale)
+    check("decode step vs fused prefill out", f64(od), f64(out[:, T - 1]), "bf16", "out")
+    check("decode step vs fused prefill lse", f64(ld), f64(lse[:, :, T - 1]), "bf16", "lse")
+    # the appended key is the forward's k' for that token
+    assert torch.equal(kc[:, T - 1], kp[:, T - 1])
+
+
+@pytest.mark.parametrize("w", [1024, 0])
+def test_decode_step_at_the_decode_config(gpu, w):
+    # The decode workload's shape as the bench times the step: 64 rows,
+    # H = Hkv = 10, D = 128, T_max = 2048, n = lengths - 1 with lengths uniform
+    # on 1..2048; the slots past the new token and before its window are NaN.
+    import torch
+    from transformer_attention_06_amd import native
+    from transformer_attention_06_amd.workload import workloads
+    wl = workloads()["decode_bf16"]
+    B, H, Hkv, D, T_max = wl.B, wl.H, wl.Hkv, wl.D, wl.T
+    print("decode step at the decode config, window", w, flush=True)
+    n = (synth.seqlens_np(B, T_max, 2000) - 1).astype(np.int32)
+    q = synth.normal_device((B, H, D), 2001, "bf16")
+    kn = synth.normal_device((B, Hkv, D), 2004, "bf16")
+    vn = synth.normal_device((B, Hkv, D), 2005, "bf16")
+    kc = synth.normal_device((B, T_max, Hkv, D), 2002, "bf16")
+    vc = synth.normal_device((B, T_max, Hkv, D), 2003, "bf16")
+    pos = torch.arange(T_max, device="cuda")[None, :]
+    nd = torch.from_numpy(n.astype(np.int64)).cuda()[:, None]
+    bad = pos > nd
+    if w > 0:
+        bad |= pos < nd + 1 - w
+    kc[bad] = float("nan")
+    vc[bad] = float("nan")
+    kc0 = kc.clone()
+    ro, rl, rkc, _ = oracle.decode_step(f64(q), f64(kn), f64(vn), f64(kc), f64(vc), n, w, wl.scale, EPS,
+                                        cache_dtype="bf16")
+    c, s = native.nc_rope_table(T_max, D)
+    out, lse = native.nc_attn_decode_step(q, kn, vn, kc, vc, torch.from_numpy(n).cuda(), c, s, EPS, w, wl.scale)
+    check(f"decode config w{w} out", f64(out), ro, "bf16", "out")
+    check(f"decode config w{w} lse", f64(lse), rl, "bf16", "lse")
+    ar = torch.arange(B, device="cuda")
+    check(f"decode config w{w} appended k'", f64(kc[ar, nd[:, 0]]), rkc[np.arange(B), n], "bf16", "out")
+    assert torch.equal(vc[ar, nd[:, 0]], vn)
+    keep = torch.ones((B, T_max), dtype=torch.bool, device="cuda")
+    keep[ar, nd[:, 0]] = False
+    assert torch.equal(kc[keep].view(torch.int16), kc0[keep].view(torch.int16))

@@ -80,8 +80,11 @@ def test_fused_matches_the_two_calls(gpu):
 
 @pytest.mark.parametrize("w", [1024, FULL])
 def test_fused_d20_full_size_sampled_rows(gpu, w):
-    """d20 at full size in the bench's configuration (prologue positions
-    0..T-1), sampled batch rows against the oracle's composition."""
+    """d20 at full size through the two calls the bench times, in its launch
+    configuration: nc_attn_fwd_prologue (the keys' prologue kernel, then the
+    forward applying the queries' prologue as it loads them) and
+    nc_attn_bwd_prologue fed by its outputs. Sampled batch rows against the
+    oracle's composition from the raw inputs (its own q', k' rounded to bf16)."""
     import torch
     from transformer_attention_06_amd import native
     wl = workloads()["d20_bf16"]
@@ -92,14 +95,19 @@ def test_fused_d20_full_size_sampled_rows(gpu, w):
     v = synth.normal_device((B, T, Hkv, D), seed + 2, "bf16")
     do = synth.normal_device((B, T, H, D), seed + 3, "bf16")
     c, s = native.nc_rope_table(10 * T, D)
-    qp, kp = native.nc_qk_prologue_fwd(q, k, c, s, EPS)
-    out, lse = native.nc_attn_fwd(qp, kp, v, w, wl.scale)
+    qp, kp, out, lse = native.nc_attn_fwd_prologue(q, k, v, c, s, EPS, w, wl.scale)
     dq, dk, dv = native.nc_attn_bwd_prologue(qp, kp, v, out, lse, do, w, wl.scale, q, k, c, s, EPS)
     torch.cuda.synchronize()
     rows = [0, B - 1]
     print("d20 window", w, "rows", rows, flush=True)
     pos = oracle.positions_from_offsets(len(rows), T)
-    rq, rk = (oracle.round_to(x, "bf16") for x in oracle.qk_prologue_fwd(f64(q[rows]), f64(k[rows]), pos, EPS))
+    rq, rk = oracle.qk_prologue_fwd(f64(q[rows]), f64(k[rows]), pos, EPS)
+    check(f"d20 w{w} q'", f64(qp[rows]), rq, "bf16", "out")
+    check(f"d20 w{w} k'", f64(kp[rows]), rk, "bf16", "out")
+    rq, rk = oracle.round_to(rq, "bf16"), oracle.round_to(rk, "bf16")
+    ro, rl = oracle.attn_fwd(rq, rk, f64(v[rows]), w, wl.scale)
+    check(f"d20 w{w} out", f64(out[rows]), ro, "bf16", "out")
+    check(f"d20 w{w} lse", f64(lse[rows]), rl, "bf16", "lse")
     gqp, gkp, gv = oracle.attn_bwd(rq, rk, f64(v[rows]), f64(do[rows]), w, wl.scale)
     gq, gk = oracle.qk_prologue_bwd(f64(q[rows]), f64(k[rows]), pos, gqp, gkp, EPS)
     check(f"d20 w{w} dq", f64(dq[rows]), gq, "bf16", "grad")

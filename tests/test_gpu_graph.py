@@ -73,3 +73,59 @@ def test_captured_layer_replays_match_eager(gpu):
                                b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (rep, n)
         run(other, q2, k2, v2)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_captured_decode_step_replays_match_eager(gpu):
+    # nc_attn_decode_step writes the new token into the caches in place: the
+    # caches are restored (eagerly) before every replay, and each replay must
+    # give the eager out, lse and caches bit for bit
+    import torch
+    from transformer_attention_06_amd import native
+    B, H, Hkv, D, T_max, w, scale = 5, 8, 2, 128, 700, 256, 0.0884
+    dt = native.NC_BF16
+    q, kn, vn, kc0, vc0 = inputs([(B, H, D), (B, Hkv, D), (B, Hkv, D), (B, T_max, Hkv, D), (B, T_max, Hkv, D)],
+                                 960, "bf16")
+    cos, sin = native.nc_rope_table(T_max, D)
+    n = torch.from_numpy(np.array([0, 63, 64, 300, T_max - 1], np.int32)).cuda()
+    ws = torch.empty(native.nc_attn_decode_step_workspace_bytes(dt, B, H, Hkv, D, T_max), dtype=torch.uint8,
+                     device="cuda")
+
+    def state():
+        return dict(kc=kc0.clone(), vc=vc0.clone(), od=torch.empty(B, H, D, dtype=torch.bfloat16, device="cuda"),
+                    ld=torch.empty(B, H, device="cuda"))
+
+    def run(x):
+        native.nc_attn_decode_step(q, kn, vn, x["kc"], x["vc"], n, cos, sin, EPS, w, scale, out=x["od"],
+                                   lse=x["ld"], workspace=ws)
+
+    names = ("kc", "vc", "od", "ld")
+    eager = state()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(eager)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    cap = state()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(cap)
+    torch.cuda.synchronize()
+    other = state()
+    for rep in range(3):
+        print("decode step replay", rep, flush=True)
+        cap["kc"].copy_(kc0)
+        cap["vc"].copy_(vc0)
+        cap["od"].fill_(float("nan"))
+        cap["ld"].fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for nm in names:
+            a, b = cap[nm], eager[nm]
+            assert torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                               b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32)), (rep, nm)
+        other["kc"].copy_(kc0)
+        other["vc"].copy_(vc0)
+        run(other)  # eager work between replays (same workspace, ordered on this stream)
+        torch.cuda.synchronize()

@@ -52,19 +52,21 @@ def test_random_shape(gpu, seed):
     rq, rk = oracle.qk_prologue_fwd(f64(q), f64(k), positions, EPS)
     check(tag + " q'", f64(qp), rq, dtype, "out")
     check(tag + " k'", f64(kp), rk, dtype, "out")
-    # attention and its backward read q', k' as stored in the dtype
-    ro, rl = oracle.attn_fwd(f64(qp), f64(kp), f64(v), w, scale)
+    # the oracle's own q', k' from the raw inputs, stored in the dtype as
+    # activations of the model are, feed its attention and backward
+    rq, rk = oracle.round_to(rq, dtype), oracle.round_to(rk, dtype)
+    ro, rl = oracle.attn_fwd(rq, rk, f64(v), w, scale)
     check(tag + " out", f64(out), ro, dtype, "out")
     check(tag + " lse", f64(lse), rl, dtype, "lse")
-    gq, gk, gv = oracle.attn_bwd(f64(qp), f64(kp), f64(v), f64(do), w, scale)
+    gq, gk, gv = oracle.attn_bwd(rq, rk, f64(v), f64(do), w, scale)
     rdq, rdk = oracle.qk_prologue_bwd(f64(q), f64(k), positions, gq, gk, EPS)
     check(tag + " dq", f64(dq), rdq, dtype, "grad")
     check(tag + " dk", f64(dk), rdk, dtype, "grad")
     check(tag + " dv", f64(dv), gv, dtype, "grad")
-    # decode: one query per row against k', v taken as a cache of T slots
+    # decode: one query per row against the raw k, v taken as a cache of T slots
     qd = q[:, 0].contiguous()
-    od, ld = native.nc_attn_decode(qd, kp, v, torch.from_numpy(c["lens"]).cuda(), w, scale)
-    rod, rld = oracle.decode(f64(qd), f64(kp), f64(v), c["lens"], w, scale)
+    od, ld = native.nc_attn_decode(qd, k, v, torch.from_numpy(c["lens"]).cuda(), w, scale)
+    rod, rld = oracle.decode(f64(qd), f64(k), f64(v), c["lens"], w, scale)
     check(tag + " decode out", f64(od), rod, dtype, "out")
     check(tag + " decode lse", f64(ld), rld, dtype, "lse")
     if dtype == "bf16" and D in (64, 128):
