@@ -29,6 +29,14 @@ import os
 import sys
 import time
 
+# Host threads for the oracle baseline: the CPUs this process may run on,
+# capped by OMP_NUM_THREADS where the environment sets it; the BLAS pools
+# are sized before numpy loads.
+AFFINITY_CPUS = len(os.sched_getaffinity(0))
+CPU_THREADS = max(1, min(AFFINITY_CPUS, int(os.environ.get("OMP_NUM_THREADS", AFFINITY_CPUS) or AFFINITY_CPUS)))
+for _v in ("OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "OMP_NUM_THREADS"):
+    os.environ.setdefault(_v, str(CPU_THREADS))
+
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 NOMINAL_SCLK_MHZ = 2400.0  # the shader clock that peak is quoted at
 PEAK_FP8_TFLOPS = 5000.0  # MI355X dense fp8 MFMA
@@ -71,6 +79,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the d12, GQA and tiny rows")
     return ap.parse_args()
 
 
@@ -234,30 +243,39 @@ def main():
     flops_f = attn_flops(B, T, H, D, wl.windows, "fwd")
     flops_b = attn_flops(B, T, H, D, wl.windows, "bwd")
     value = (flops_f + flops_b) / (ms_step * 1e-3) / 1e12
-    # flops each kernel performs per step: the forward 4*D per visible pair;
-    # the whole backward is counted as 8*D per pair (dV, dK, dQ and the dP
-    # product); its dK/dV kernel executes 8*D (S, dP, dV, dK) and its dQ
-    # kernel 6*D (S and dP again, then dQ)
-    kflops = {"attn_fwd": flops_f, "attn_bwd": flops_b, "attn_bwd_dkdv": flops_b,
-              "attn_bwd_dq": attn_flops(B, T, H, D, wl.windows, "fwd") * 3 // 2}
+    # Algorithmic (band-counted) flops per visible pair of each unit: the
+    # forward 4*D; the whole backward 8*D = the dV, dP, dK and dQ products,
+    # of which the dK/dV kernel produces dV, dP and dK (6*D) and the dQ
+    # kernel dQ (2*D), so the two kernels' shares add up to the backward's.
+    # Executed flops differ: the dK/dV kernel also recomputes S (8*D), the
+    # dQ kernel recomputes S and dP (6*D); those rates are reported apart.
+    ALG = {"attn_fwd": 4, "attn_bwd": 8, "attn_bwd_dkdv": 6, "attn_bwd_dq": 2}
+    EXE = {"attn_fwd": 4, "attn_bwd": 14, "attn_bwd_dkdv": 8, "attn_bwd_dq": 6}
+
+    def kf(name, windows, table):  # flops of one unit over the given layers
+        return attn_flops(B, T, H, D, windows, "fwd") // 4 * table[name]
+
     kern, per_window = {}, {}
     for label, (ms, n) in tot.items():
         if "@" in label:  # one layer type: per-launch time and its own band-counted rate
             name, tag = label.split("@")
             w = FULL if tag == "full" else int(tag)
-            f1 = attn_flops(B, T, H, D, [w], "fwd")
-            lf = {"attn_fwd": f1, "attn_bwd": 2 * f1, "attn_bwd_dkdv": 2 * f1, "attn_bwd_dq": f1 * 3 // 2}[name]
             per_ms = ms / n
+            alg = kf(name, [w], ALG) / (per_ms * 1e-3) / 1e12
+            exe = kf(name, [w], EXE) / (per_ms * 1e-3) / 1e12
             per_window.setdefault(tag, {})[name] = {
-                "avg_ms_per_launch": round(per_ms, 5), "tflops": round(lf / (per_ms * 1e-3) / 1e12, 2),
-                "frac_bf16_peak": round(lf / (per_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                "avg_ms_per_launch": round(per_ms, 5), "tflops": round(alg, 2),
+                "frac_bf16_peak": round(alg / PEAK_BF16_TFLOPS, 4), "executed_tflops": round(exe, 2),
+                "executed_frac_bf16_peak": round(exe / PEAK_BF16_TFLOPS, 4)}
             continue
         per_step = ms / args.steps
         row = {"ms_per_step": round(per_step, 4), "launches_per_step": n // args.steps,
                "avg_ms_per_launch": round(ms / n, 5)}
-        if label in kflops:
-            row["tflops"] = round(kflops[label] / (per_step * 1e-3) / 1e12, 2)
+        if label in ALG:
+            row["tflops"] = round(kf(label, wl.windows, ALG) / (per_step * 1e-3) / 1e12, 2)
             row["frac_bf16_peak"] = round(row["tflops"] / PEAK_BF16_TFLOPS, 4)
+            row["executed_tflops"] = round(kf(label, wl.windows, EXE) / (per_step * 1e-3) / 1e12, 2)
+            row["executed_frac_bf16_peak"] = round(row["executed_tflops"] / PEAK_BF16_TFLOPS, 4)
         if label == "prologue_fwd_k":  # reads k, writes k'
             nbytes = 2 * L * (B * T * Hkv * D * 2)
             row["gbs"] = round(nbytes / (per_step * 1e-3) / 1e9, 1)
@@ -370,7 +388,7 @@ def main():
 
     # ------------------------------------------------------------- roofline
     dom = max(("attn_fwd", "attn_bwd_dkdv", "attn_bwd_dq"), key=lambda k: kern[k]["ms_per_step"])
-    dom_flops = kflops[dom]
+    dom_flops = kf(dom, wl.windows, ALG)
     n_launch = kern[dom]["launches_per_step"]
     achieved = dom_flops / n_launch / (kern[dom]["avg_ms_per_launch"] * 1e-3) / 1e12
     tr = measured_traffic(dom)
@@ -382,14 +400,28 @@ def main():
                 "peak_at_sclk": round(PEAK_BF16_TFLOPS * sclk_mhz / NOMINAL_SCLK_MHZ, 1) if sclk_mhz else None,
                 "frac_at_sclk": round(achieved / (PEAK_BF16_TFLOPS * sclk_mhz / NOMINAL_SCLK_MHZ), 4)
                 if sclk_mhz else None,
-                "note": "achieved = band-counted flops per launch (per visible pair: 4*D fwd, "
-                        "8*D dK/dV kernel, 6*D dQ kernel; B*H*pairs(T,w) pairs) / average launch "
-                        "time, averaged over the 20 layers"}
+                "flops_per_launch": dom_flops // n_launch,
+                "note": "achieved = algorithmic band-counted flops per launch (per visible pair: 4*D "
+                        "forward; of the backward's 8*D, 6*D for the dK/dV kernel (dV, dP, dK) and 2*D "
+                        "for the dQ kernel (dQ); B*H*pairs(T,w) pairs) / average launch time, averaged "
+                        "over the 20 layers"}
+    fractions = {
+        "attn_fwd_frac_bf16_peak": kern["attn_fwd"]["frac_bf16_peak"],
+        "attn_bwd_frac_bf16_peak": kern["attn_bwd"]["frac_bf16_peak"],
+        "decode_frac_hbm_peak": decode["frac_hbm_peak"] if decode else None,
+        "decode_step_frac_hbm_peak": decode["step_with_append"]["frac_hbm_peak"] if decode else None,
+        "targets": {"attn_fwd": 0.50, "attn_bwd": 0.35, "decode": 0.70}}
 
     # --------------------------------------------------------- cpu baseline
+    others = None
+    if not args.no_workloads:
+        del qr, kr, vv, do, qp, kp, out, lse
+        torch.cuda.empty_cache()
+        others = other_workloads(args, np, torch, native, synth, time_phase)
+
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(args, np, torch, synth, wl, qr, kr, vv, do, cos, eps, band_pairs, FULL)
+        cpu = cpu_baseline(args, np, torch, synth, wl, cos, eps, band_pairs, FULL, decode_bytes)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -411,23 +443,103 @@ def main():
         "per_window": per_window,
         "decode": decode,
         "fp8_forward": fp8,
+        "workloads": others,
+        "fractions": fractions,
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(args, np, torch, synth, wl, qr, kr, vv, do, cos, eps, band_pairs, FULL):
-    """The fp64 oracle, as it stands, on a bounded sample of the same inputs:
-    whole batch rows (all heads) of one windowed layer and one full layer,
-    prologue + attention forward + backward, alternating until the budget is
-    spent. Rate in band-counted TFLOP/s like the GPU value."""
+def other_workloads(args, np, torch, native, synth, time_phase):
+    """The other training-side configurations at their full sizes, each timed
+    as whole phases: every call's attention forward, then every call's
+    backward in reverse order (d12: 12 SSSL layers; GQA: a windowed and a
+    full call, dK/dV summed over each group of 4 query heads; both without
+    the prologue, whose inputs the configurations give directly). Tiny
+    (float32, the prologue forward and backward around each call, two
+    calls) is reported as time only: it is launch-bound by design."""
+    from transformer_attention_06_amd.workload import attn_flops, workloads
+    res = {}
+    for name in ("d12_bf16", "gqa_bf16"):
+        w = workloads()[name]
+        B, T, H, Hkv, D = w.B, w.T, w.H, w.Hkv, w.D
+        n = len(w.windows)
+        log(f"{name}: {n} calls, B={B} T={T} H={H} Hkv={Hkv} D={D}")
+        seed = 3000 if name == "d12_bf16" else 4000
+        q = [synth.normal_device((B, T, H, D), seed + 10 * l, "bf16") for l in range(n)]
+        k = [synth.normal_device((B, T, Hkv, D), seed + 10 * l + 1, "bf16") for l in range(n)]
+        v = [synth.normal_device((B, T, Hkv, D), seed + 10 * l + 2, "bf16") for l in range(n)]
+        g = [synth.normal_device((B, T, H, D), seed + 10 * l + 3, "bf16") for l in range(n)]
+        o = [torch.empty_like(x) for x in q]
+        ls = [torch.empty((B, H, T), dtype=torch.float32, device="cuda") for _ in range(n)]
+        dq, dk, dv = torch.empty_like(q[0]), torch.empty_like(k[0]), torch.empty_like(v[0])
+        ws = torch.empty(native.nc_attn_bwd_workspace_bytes(native.NC_BF16, B, T, H, Hkv, D), dtype=torch.uint8,
+                         device="cuda")
+
+        def fwd():
+            for l, win in enumerate(w.windows):
+                native.nc_attn_fwd(q[l], k[l], v[l], win, w.scale, out=o[l], lse=ls[l])
+
+        def bwd():
+            for l in reversed(range(n)):
+                native.nc_attn_bwd(q[l], k[l], v[l], o[l], ls[l], g[l], w.windows[l], w.scale, dq=dq, dk=dk, dv=dv,
+                                   workspace=ws)
+
+        fms, fsp = time_phase(fwd)
+        bms, bsp = time_phase(bwd)
+        ff, fb = attn_flops(B, T, H, D, w.windows, "fwd"), attn_flops(B, T, H, D, w.windows, "bwd")
+        res[name] = {
+            "calls": n, "windows": w.windows, "band_flops_fwd": ff, "band_flops_bwd": fb,
+            "fwd_ms": round(fms, 4), "fwd_ms_spread": fsp, "bwd_ms": round(bms, 4), "bwd_ms_spread": bsp,
+            "fwd_tflops": round(ff / (fms * 1e-3) / 1e12, 2), "bwd_tflops": round(fb / (bms * 1e-3) / 1e12, 2),
+            "fwdbwd_tflops": round((ff + fb) / ((fms + bms) * 1e-3) / 1e12, 2),
+            "fwd_frac_bf16_peak": round(ff / (fms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bwd_frac_bf16_peak": round(fb / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        log(name, json.dumps(res[name]))
+        del q, k, v, g, o, ls, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    # tiny float32 with the prologue around each call (as its configuration states)
+    w = workloads()["tiny_f32"]
+    B, T, H, Hkv, D = w.B, w.T, w.H, w.Hkv, w.D
+    q, k, v, g = (synth.normal_torch(sh, 5000 + i, "f32", "cuda") for i, sh in
+                  enumerate([(B, T, H, D), (B, T, Hkv, D), (B, T, Hkv, D), (B, T, H, D)]))
+    c, sn = native.nc_rope_table(10 * T, D)
+    eps = 2.0 ** -23
+
+    def tiny():
+        for win in w.windows:
+            qp, kp = native.nc_qk_prologue_fwd(q, k, c, sn, eps)
+            o, ls = native.nc_attn_fwd(qp, kp, v, win, w.scale)
+            dqp, dkp, _ = native.nc_attn_bwd(qp, kp, v, o, ls, g, win, w.scale)
+            native.nc_qk_prologue_bwd(q, k, c, sn, eps, dqp, dkp)
+
+    tms, tsp = time_phase(tiny)
+    res["tiny_f32"] = {"calls": len(w.windows), "windows": w.windows, "ms": round(tms, 4), "ms_spread": tsp,
+                       "what": "prologue fwd + attention fwd + bwd + prologue bwd per call, float32 "
+                               "(time only: latency-bound)"}
+    log("tiny_f32", json.dumps(res["tiny_f32"]))
+    return res
+
+
+def cpu_baseline(args, np, torch, synth, wl, cos, eps, band_pairs, FULL, decode_bytes):
+    """The fp64 oracle, as it stands, on bounded samples of the same inputs,
+    with the BLAS pools at CPU_THREADS threads:
+      * training: whole batch rows (all heads) of one windowed and one full
+        d20 layer, prologue + attention forward + backward, alternating
+        until about --cpu-seconds are spent; band-counted TFLOP/s like the
+        GPU value;
+      * decode: one windowed and one full layer of the decode workload (all
+        64 rows, the bench's seeded lengths and caches), oracle.decode
+        timed alone; GB/s over the same algorithmic bytes as the GPU's."""
     import oracle
+    from transformer_attention_06_amd.workload import workloads
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_limits, threadpool_info
+        limiter = threadpool_limits(CPU_THREADS)
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
-        threads = 1
+        limiter, threads = None, CPU_THREADS
     layers = [wl.windows.index(1024), wl.windows.index(FULL)]
     T, H, D = wl.T, wl.H, wl.D
     pos = oracle.positions_from_offsets(1, T)
@@ -436,10 +548,12 @@ def cpu_baseline(args, np, torch, synth, wl, qr, kr, vv, do, cos, eps, band_pair
     while elapsed < args.cpu_seconds and b < wl.B:
         for l in layers:
             w = wl.windows[l]
-            q = synth.to_f64(qr[l][b:b + 1])
-            k = synth.to_f64(kr[l][b:b + 1])
-            v = synth.to_f64(vv[l][b:b + 1])
-            g = synth.to_f64(do[l][b:b + 1])
+            # the bench's d20 inputs of layer l, batch row b (same seeds, drawn again)
+            q = synth.to_f64(synth.normal_device((wl.B, T, H, D), 1000 + 10 * l, "bf16")[b:b + 1])
+            k = synth.to_f64(synth.normal_device((wl.B, T, wl.Hkv, D), 1001 + 10 * l, "bf16")[b:b + 1])
+            v = synth.to_f64(synth.normal_device((wl.B, T, wl.Hkv, D), 1002 + 10 * l, "bf16")[b:b + 1])
+            g = synth.to_f64(synth.normal_device((wl.B, T, H, D), 1003 + 10 * l, "bf16")[b:b + 1])
+            torch.cuda.empty_cache()
             t = time.perf_counter()
             q1, k1 = oracle.qk_prologue_fwd(q, k, pos, eps)
             oracle.attn_fwd(q1, k1, v, w, wl.scale)
@@ -450,11 +564,38 @@ def cpu_baseline(args, np, torch, synth, wl, qr, kr, vv, do, cos, eps, band_pair
             n_rows += 1
         b += 1
         log(f"cpu baseline: {n_rows} row-layers in {elapsed:.1f} s")
+    # decode: the bench's decode inputs of one windowed and one full layer
+    dw = workloads()["decode_bf16"]
+    lens = synth.seqlens_np(dw.B, dw.T, 2000)
+    d_bytes, d_el = 0, 0.0
+    for l in (dw.windows.index(1024), dw.windows.index(FULL)):
+        w = dw.windows[l]
+        qd = synth.to_f64(synth.normal_device((dw.B, dw.H, dw.D), 2001 + 10 * l, "bf16"))
+        kc = synth.to_f64(synth.normal_device((dw.B, dw.T, dw.Hkv, dw.D), 2002 + 10 * l, "bf16"))
+        vc = synth.to_f64(synth.normal_device((dw.B, dw.T, dw.Hkv, dw.D), 2003 + 10 * l, "bf16"))
+        torch.cuda.empty_cache()
+        reps = 0
+        t = time.perf_counter()
+        while reps < 3 or time.perf_counter() - t < 1.0:  # repeated for a stable rate
+            oracle.decode(qd, kc, vc, lens, w, dw.scale)
+            reps += 1
+        d_el += time.perf_counter() - t
+        d_bytes += reps * decode_bytes(lens, dw.H, dw.Hkv, dw.D, w)
+        del kc, vc
+    log(f"cpu baseline decode: 2 layers in {d_el:.2f} s")
+    if limiter is not None:
+        limiter.unregister()
     return {"value": round(done_flops / elapsed / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "affinity_cpus": AFFINITY_CPUS,
             "kind": "oracle",
             "sample": f"{n_rows} (batch row, layer) pairs of d20 (all 10 heads, T=2048; layers with "
                       f"window 1024 and full alternating): fp64 numpy prologue + attention fwd + bwd, "
-                      f"{elapsed:.1f} s"}
+                      f"{elapsed:.1f} s",
+            "decode": {"value": round(d_bytes / d_el / 1e9, 3), "unit": "GB/s",
+                       "sample": f"oracle.decode on one windowed and one full layer of the decode workload "
+                                 f"(64 rows, lengths uniform 1..2048), each repeated for at least 1 s "
+                                 f"({d_el:.2f} s in all); rate over the GPU's algorithmic bytes of those calls "
+                                 f"({d_bytes} B)"}}
 
 
 if __name__ == "__main__":
