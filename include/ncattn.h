@@ -277,6 +277,28 @@ nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_m
                               void* workspace, size_t workspace_bytes, nc_stream stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the step
+ * of nc_attn_decode_step, same arguments, results and errors, without the
+ * workspace. Its split-K partials go to a scratch array that the library
+ * holds on each GPU it runs on (NC_NOALLOC_SCRATCH_BYTES, placed when the
+ * library's code is loaded on that GPU and kept until the process ends);
+ * this call allocates nothing. Sizes whose partials
+ * (nc_attn_decode_step_workspace_bytes) exceed that array give
+ * NC_ERR_UNSUPPORTED with nothing launched. Every call on a GPU shares that
+ * GPU's array and leaves its partials there: calls that may overlap on one
+ * GPU (e.g. on two streams without ordering between them) race and must not
+ * be issued; calls ordered on one stream are safe. Nothing in the array
+ * needs to start at zero (each call writes every partial it reads).
+ */
+#define NC_NOALLOC_SCRATCH_BYTES (32u << 20)
+nc_status nc_attn_decode_step_noalloc(nc_dtype dt, int B, int H, int Hkv, int D, int T_max,
+                                      const void* q, const void* k_new, const void* v_new,
+                                      void* k_cache, void* v_cache, const int32_t* cache_seqlens,
+                                      const float* cos_tab, const float* sin_tab, int T_rope, float eps,
+                                      int window, float scale, void* out, float* lse, nc_stream stream);
+
+/*
  * Expands a batch-1 prefill cache into a decode cache of n_rows rows, so the
  * prompt is processed once ("nanochat Admin & Developer Guide", section 7
  * "KV cache" and "Generation flow": prefill once, then replicate the cache

@@ -266,6 +266,28 @@ def test_decode_step_validation(L):
     assert dstep(L, wsb=100) == WORKSPACE
 
 
+def dstep_noalloc(L, B=2, H=4, Hkv=2, D=64, T_max=100, k_new=A, lens=A, eps=1e-6, scale=0.1):
+    return L.nc_attn_decode_step_noalloc(BF16, B, H, Hkv, D, T_max, A, k_new, A, A, A, lens, A, A, 128, eps, 0,
+                                         scale, A, A, None)
+
+
+def test_decode_step_noalloc_validation(L):
+    # the same checks as nc_attn_decode_step, and a size limit instead of a workspace
+    assert dstep_noalloc(L, H=5, Hkv=1) == UNSUPPORTED
+    assert dstep_noalloc(L, k_new=None) == INVALID
+    assert dstep_noalloc(L, lens=A + 2) == INVALID
+    assert dstep_noalloc(L, eps=float("nan")) == INVALID
+    assert dstep_noalloc(L, scale=0.0) == INVALID
+    need = L.nc_attn_decode_step_workspace_bytes(BF16, 64, 32, 4, 128, 4096)
+    assert need > native.NC_NOALLOC_SCRATCH_BYTES
+    assert dstep_noalloc(L, B=64, H=32, Hkv=4, D=128, T_max=4096) == UNSUPPORTED
+    assert "scratch" in msg(L)
+    # the decode workload's partials fit
+    assert L.nc_attn_decode_step_workspace_bytes(BF16, 64, 10, 10, 128, 2048) <= native.NC_NOALLOC_SCRATCH_BYTES
+    if not _gpu():
+        assert dstep_noalloc(L, B=64, H=10, Hkv=10, D=128, T_max=2048) == DEVICE
+
+
 def test_kv_cache_replicate_validation(L):
     f = L.nc_kv_cache_replicate
     assert f(BF16, 4, 100, 2, 64, 0, A, A, None) == INVALID  # n_tokens < 1

@@ -358,11 +358,14 @@ size_t nc_attn_decode_step_workspace_bytes(nc_dtype dt, int B, int H, int Hkv, i
   return nc_attn_decode_workspace_bytes(dt, B, H, Hkv, D, T_max);  // the split-K partials only
 }
 
-nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q,
-                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
-                              const int32_t* cache_seqlens, const float* cos_tab, const float* sin_tab, int T_rope,
-                              float eps, int window, float scale, void* out, float* lse, void* workspace,
-                              size_t workspace_bytes, nc_stream stream) {
+namespace {
+
+// Validation shared by the two decode-step entry points (everything but the
+// workspace).
+nc_status decode_step_checks(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q,
+                             const void* k_new, const void* v_new, const void* k_cache, const void* v_cache,
+                             const int32_t* cache_seqlens, const float* cos_tab, const float* sin_tab, int T_rope,
+                             float eps, float scale, const void* out, const float* lse) {
   NC_TRY(check_shape(dt, B, T_max, H, Hkv, D));
   if ((long long)B * T_max * Hkv * D > kMaxElems)
     return fail(NC_ERR_UNSUPPORTED, "cache of B*T_max*Hkv*D elements exceeds 2^31-1");
@@ -384,17 +387,83 @@ nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_m
   if (!lse) return fail(NC_ERR_INVALID_ARG, "lse is NULL");
   if (((uintptr_t)lse & 3u) != 0) return fail(NC_ERR_INVALID_ARG, "lse is not 4-byte aligned");
   NC_TRY(check_scale(scale));
-  const size_t need = nc_attn_decode_step_workspace_bytes(dt, B, H, Hkv, D, T_max);
-  if (!workspace || !aligned16(workspace) || workspace_bytes < need)
-    return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
-  NC_TRY(check_device(nullptr));
+  return NC_OK;
+}
+
+nc_status decode_step_launch(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q, const void* k_new,
+                             const void* v_new, void* k_cache, void* v_cache, const int32_t* cache_seqlens,
+                             const float* cos_tab, const float* sin_tab, int T_rope, float eps, int window,
+                             float scale, void* out, float* lse, float* part, nc_stream stream, const char* what) {
   // the split kernel applies the prologue and writes the cache slot itself
-  nc::DecodeParams p{q, k_cache, v_cache, cache_seqlens, out, lse, (float*)workspace, B, H, Hkv, D, T_max,
+  nc::DecodeParams p{q, k_cache, v_cache, cache_seqlens, out, lse, part, B, H, Hkv, D, T_max,
                      window <= 0 ? 0 : window, decode_splits(T_max, D, H / Hkv), scale,
                      scale * 1.4426950408889634f, 1, k_new, v_new, cos_tab, sin_tab, T_rope, eps};
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = nc::launch_decode(p, dt == NC_BF16, s);
-  return finish(e, s, "nc_attn_decode_step");
+  return finish(e, s, what);
+}
+
+// Scratch of the entry point that allocates nothing: a file-scope device
+// array, one copy per GPU (the runtime places it when it loads this code
+// object on a device and keeps it until the process ends). In host code the
+// array's name is only a stand-in for the symbol; its device address differs
+// per GPU and comes from hipGetSymbolAddress, taken once per device with that
+// device current and cached here. Every use passes that address.
+static __device__ __align__(256) unsigned char scratch[NC_NOALLOC_SCRATCH_BYTES];
+
+nc_status scratch_ptr(int dev, void** out) {
+  static std::mutex mu;
+  static void* ptrs[64];
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptrs[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return fail(NC_ERR_DEVICE, "scratch: hipGetSymbolAddress failed on device %d: %s", dev, hipGetErrorString(e));
+    }
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return NC_OK;
+}
+
+}  // namespace
+
+nc_status nc_attn_decode_step(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q,
+                              const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* cache_seqlens, const float* cos_tab, const float* sin_tab, int T_rope,
+                              float eps, int window, float scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, nc_stream stream) {
+  NC_TRY(decode_step_checks(dt, B, H, Hkv, D, T_max, q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos_tab,
+                            sin_tab, T_rope, eps, scale, out, lse));
+  const size_t need = nc_attn_decode_step_workspace_bytes(dt, B, H, Hkv, D, T_max);
+  if (!workspace || !aligned16(workspace) || workspace_bytes < need)
+    return fail(NC_ERR_WORKSPACE, "workspace needs %zu bytes (16-byte aligned), got %zu", need, workspace_bytes);
+  NC_TRY(check_device(nullptr));
+  return decode_step_launch(dt, B, H, Hkv, D, T_max, q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos_tab,
+                            sin_tab, T_rope, eps, window, scale, out, lse, (float*)workspace, stream,
+                            "nc_attn_decode_step");
+}
+
+nc_status nc_attn_decode_step_noalloc(nc_dtype dt, int B, int H, int Hkv, int D, int T_max, const void* q,
+                                      const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                      const int32_t* cache_seqlens, const float* cos_tab, const float* sin_tab,
+                                      int T_rope, float eps, int window, float scale, void* out, float* lse,
+                                      nc_stream stream) {
+  NC_TRY(decode_step_checks(dt, B, H, Hkv, D, T_max, q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos_tab,
+                            sin_tab, T_rope, eps, scale, out, lse));
+  const size_t need = nc_attn_decode_step_workspace_bytes(dt, B, H, Hkv, D, T_max);
+  if (need > (size_t)NC_NOALLOC_SCRATCH_BYTES)
+    return fail(NC_ERR_UNSUPPORTED, "these sizes need %zu bytes of scratch; the library's scratch holds %zu",
+                need, (size_t)NC_NOALLOC_SCRATCH_BYTES);
+  int dev = -1;
+  NC_TRY(check_device(&dev));
+  void* part = nullptr;
+  NC_TRY(scratch_ptr(dev, &part));
+  return decode_step_launch(dt, B, H, Hkv, D, T_max, q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos_tab,
+                            sin_tab, T_rope, eps, window, scale, out, lse, (float*)part, stream,
+                            "nc_attn_decode_step_noalloc");
 }
 
 nc_status nc_kv_cache_replicate(nc_dtype dt, int n_rows, int T_max, int Hkv, int D, int n_tokens, const void* src,

@@ -25,7 +25,8 @@ EXPORTS = (
     "nc_attn_fwd", "nc_attn_fwd_cache", "nc_kv_cache_append", "nc_attn_bwd_workspace_bytes", "nc_attn_bwd", "nc_attn_bwd_prologue",
     "nc_profile_bwd_main",
     "nc_attn_decode_workspace_bytes", "nc_attn_decode",
-    "nc_attn_decode_step_workspace_bytes", "nc_attn_decode_step", "nc_kv_cache_replicate",
+    "nc_attn_decode_step_workspace_bytes", "nc_attn_decode_step", "nc_attn_decode_step_noalloc",
+    "nc_kv_cache_replicate",
     "nc_rope_table", "nc_qk_prologue_fwd", "nc_qk_prologue_bwd", "nc_attn_fwd_prologue",
     "nc_profile_fwd_prologue", "nc_measure_shader_clock", "nc_attn_fwd_fp8",
 )
@@ -59,6 +60,7 @@ _SIGS = {
     "nc_attn_decode": ([_i] * 6 + [_p] * 4 + [_i, _f, _p, _p, _p, _sz, _p], _i),
     "nc_attn_decode_step_workspace_bytes": ([_i] * 6, _sz),
     "nc_attn_decode_step": ([_i] * 6 + [_p] * 8 + [_i, _f, _i, _f, _p, _p, _p, _sz, _p], _i),
+    "nc_attn_decode_step_noalloc": ([_i] * 6 + [_p] * 8 + [_i, _f, _i, _f, _p, _p, _p], _i),
     "nc_kv_cache_replicate": ([_i] * 6 + [_p, _p, _p], _i),
     "nc_rope_table": ([_i, _i, _d, _p, _p, _p], _i),
     "nc_qk_prologue_fwd": ([_i] * 6 + [_p] * 5 + [_i, _f, _p, _p, _p], _i),
@@ -373,6 +375,31 @@ def nc_attn_decode_step(q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos, s
                                    _arg(lse, "lse", (B, H), (torch.float32,), dev),
                                    _arg(workspace, "workspace", None, None, dev), _nbytes(workspace), _stream(stream))
     _raise_on("nc_attn_decode_step", st)
+    return out, lse
+
+
+NC_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def nc_attn_decode_step_noalloc(q, k_new, v_new, k_cache, v_cache, cache_seqlens, cos, sin, eps, window, scale,
+                                out, lse, stream=None):
+    """nc_attn_decode_step without a workspace (the library's per-GPU scratch holds the split-K
+    partials): out [B,H,D] and lse [B,H] must be given, nothing is allocated here either."""
+    import torch
+    dev = _gpu(q, "q")
+    B, H, D = _dims(q, "q", 3)
+    T_max, Hkv = _dims(k_cache, "k_cache", 4)[1:3]
+    dt, cs = (q.dtype,), (B, T_max, Hkv, D)
+    c, s_, T_rope = _rope_args(cos, sin, D, dev)
+    st = lib().nc_attn_decode_step_noalloc(_dt(q), B, H, Hkv, D, T_max, _arg(q, "q", None, None, dev),
+                                           _arg(k_new, "k_new", (B, Hkv, D), dt, dev),
+                                           _arg(v_new, "v_new", (B, Hkv, D), dt, dev),
+                                           _arg(k_cache, "k_cache", cs, dt, dev), _arg(v_cache, "v_cache", cs, dt, dev),
+                                           _arg(cache_seqlens, "cache_seqlens", (B,), (torch.int32,), dev), c, s_,
+                                           T_rope, float(eps), int(window), float(scale),
+                                           _arg(out, "out", (B, H, D), dt, dev),
+                                           _arg(lse, "lse", (B, H), (torch.float32,), dev), _stream(stream))
+    _raise_on("nc_attn_decode_step_noalloc", st)
     return out, lse
 
 
